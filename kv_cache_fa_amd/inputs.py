@@ -1,0 +1,300 @@
+"""Seeded synthetic inputs for exact attention: prefill tensors and a paged KV cache.
+
+This module is shared by the HIP path (tests, bench) and by the fp64 CPU oracle's
+tests. It draws random numbers, rounds them to the storage type and lays them out
+in memory; it holds none of the attention arithmetic. Everything here is NumPy.
+
+Workloads (shapes follow the problem statement of the page "Donanıma Duyarlı
+Algoritma Tasarımı: FlashAttention", section "Transformer Mimarisi ve
+Self-Attention Mekanizması": Q, K and V are (sequence length x dimension) per
+head; the KV-cache and GQA structure follows the glossary entry "KV Cache
+(Anahtar-Değer Önbelleği)" on the yapayzekasozluk.tr "Attention" tag page):
+
+  fp32_single   B=1 H=1  Hkv=1 N=128    d=64  non-causal fp32, N(0,1)
+  bf16_causal   B=2 H=8  Hkv=8 N=1024   d=64  causal bf16, N(0,1) x 0.5
+  gqa_causal    B=4 H=32 Hkv=8 N=4096   d=128 causal bf16, N(0,1)
+  paged_decode  64 sequences x 1 query, H=32 Hkv=8 d=128, KV length ~ U{512..8192},
+                pages of 16 tokens, seeded random permutation page table
+  long_causal   B=1 H=8  Hkv=8 N=131072 d=128 causal bf16, N(0,1) x 0.5
+
+Draw order for a prefill workload (one ``numpy.random.default_rng(seed)``):
+Q, K, V, each ``standard_normal(dtype=float32)`` in [B, H(kv), N, d] order, then
+multiplied by ``value_scale`` (exact: a power of two), then rounded to bf16 with
+round-to-nearest-even. Row samples (for the large workloads) are drawn afterwards
+from the same generator.
+
+Draw order for the paged decode workload: sequence lengths, then the physical page
+permutation, then Q, then K_s and V_s for s = 0..num_seqs-1.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+BF16_NAN_BITS = np.uint16(0x7FC0)
+
+
+# ----------------------------------------------------------------------------------
+# bf16 storage helpers (bit patterns held in uint16 arrays)
+# ----------------------------------------------------------------------------------
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 with round-to-nearest, ties to even.
+
+    Returns the 16-bit patterns as uint16. NaN inputs are not expected (the
+    generators draw finite normals); they are mapped to the canonical quiet NaN.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32)
+    lsb = (bits >> np.uint32(16)) & np.uint32(1)
+    rounded = (bits + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = BF16_NAN_BITS
+    return out
+
+
+def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 exactly (bf16 is the top half of fp32)."""
+    u = np.ascontiguousarray(u, dtype=np.uint16)
+    return (u.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_bits_to_f64(u: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float64 exactly."""
+    return bf16_bits_to_f32(u).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------------
+# Prefill workloads
+# ----------------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class PrefillConfig:
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    dtype: str            # "f32" or "bf16"
+    value_scale: float    # N(0,1) draws are multiplied by this before rounding
+    scale: float          # softmax scale applied to Q.K^T
+    seed: int
+
+    @property
+    def flops(self) -> float:
+        """Algorithmic flops: 4*d per unmasked (query, key) pair (Q.K^T and P.V)."""
+        return 4.0 * self.d * self.B * self.H * unmasked_pairs(self.Nq, self.Nk, self.causal)
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    num_seqs: int
+    H: int
+    Hkv: int
+    d: int
+    len_lo: int
+    len_hi: int           # inclusive
+    page_size: int
+    max_seq_len: int
+    scale: float
+    seed: int
+
+
+def unmasked_pairs(Nq: int, Nk: int, causal: bool) -> int:
+    """Number of (query, key) pairs that attend, per (batch, head).
+
+    Causal uses bottom-right alignment: query i sits at absolute position Nk-Nq+i.
+    """
+    if not causal:
+        return Nq * Nk
+    off = Nk - Nq
+    # sum_{i=0}^{Nq-1} (i + off + 1)
+    return Nq * (off + 1) + Nq * (Nq - 1) // 2
+
+
+PREFILL_CONFIGS = {
+    "fp32_single": PrefillConfig("fp32_single", 1, 1, 1, 128, 128, 64, False, "f32",
+                                 1.0, 1.0 / math.sqrt(64), 1),
+    "bf16_causal": PrefillConfig("bf16_causal", 2, 8, 8, 1024, 1024, 64, True, "bf16",
+                                 0.5, 1.0 / math.sqrt(64), 2),
+    "gqa_causal": PrefillConfig("gqa_causal", 4, 32, 8, 4096, 4096, 128, True, "bf16",
+                                1.0, 1.0 / math.sqrt(128), 3),
+    "long_causal": PrefillConfig("long_causal", 1, 8, 8, 131072, 131072, 128, True, "bf16",
+                                 0.5, 1.0 / math.sqrt(128), 5),
+}
+
+DECODE_CONFIGS = {
+    "paged_decode": DecodeConfig("paged_decode", 64, 32, 8, 128, 512, 8192, 16, 8192,
+                                 1.0 / math.sqrt(128), 4),
+}
+
+
+@dataclasses.dataclass
+class PrefillInputs:
+    cfg: PrefillConfig
+    q: np.ndarray   # [B,H,Nq,d]   float32 (f32) or uint16 bf16 bits
+    k: np.ndarray   # [B,Hkv,Nk,d]
+    v: np.ndarray   # [B,Hkv,Nk,d]
+    rng: np.random.Generator  # positioned after V, for row samples
+
+    def as_f64(self):
+        """The stored values widened exactly to float64 (what the oracle consumes)."""
+        if self.cfg.dtype == "f32":
+            return (self.q.astype(np.float64), self.k.astype(np.float64),
+                    self.v.astype(np.float64))
+        return bf16_bits_to_f64(self.q), bf16_bits_to_f64(self.k), bf16_bits_to_f64(self.v)
+
+
+def _draw(rng: np.random.Generator, shape, value_scale: float, dtype: str) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if value_scale != 1.0:
+        x *= np.float32(value_scale)
+    if dtype == "f32":
+        return x
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def make_prefill(cfg: PrefillConfig, seed: int | None = None) -> PrefillInputs:
+    """Draw Q, K, V for a prefill workload (see the module docstring for the order)."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    q = _draw(rng, (cfg.B, cfg.H, cfg.Nq, cfg.d), cfg.value_scale, cfg.dtype)
+    k = _draw(rng, (cfg.B, cfg.Hkv, cfg.Nk, cfg.d), cfg.value_scale, cfg.dtype)
+    v = _draw(rng, (cfg.B, cfg.Hkv, cfg.Nk, cfg.d), cfg.value_scale, cfg.dtype)
+    return PrefillInputs(cfg, q, k, v, rng)
+
+
+def custom_prefill(B, H, Hkv, Nq, Nk, d, causal, dtype="bf16", value_scale=1.0,
+                   scale=None, seed=0, name="custom") -> PrefillInputs:
+    """Any shape, same recipe (used for ragged tails and edge cases)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    cfg = PrefillConfig(name, B, H, Hkv, Nq, Nk, d, causal, dtype, value_scale, scale, seed)
+    return make_prefill(cfg)
+
+
+def sample_rows(inp: PrefillInputs, n_full_pairs: int, n_random_rows: int):
+    """Seeded row selection for workloads too large to check in full.
+
+    Returns a dict {(b, h): sorted int64 array of query rows}. ``n_full_pairs``
+    (b, h) pairs are checked on every row; ``n_random_rows`` further rows are drawn
+    uniformly without replacement from the remaining (b, h, i) triples.
+    """
+    cfg = inp.cfg
+    rng = inp.rng
+    BH = cfg.B * cfg.H
+    full = rng.choice(BH, size=min(n_full_pairs, BH), replace=False)
+    sel: dict[tuple[int, int], np.ndarray] = {}
+    for p in sorted(int(x) for x in full):
+        sel[(p // cfg.H, p % cfg.H)] = np.arange(cfg.Nq, dtype=np.int64)
+    if n_random_rows:
+        rest = np.setdiff1d(np.arange(BH), full)
+        if rest.size:
+            total = rest.size * cfg.Nq
+            flat = rng.choice(total, size=min(n_random_rows, total), replace=False)
+            pair = rest[flat // cfg.Nq]
+            row = flat % cfg.Nq
+            for p in np.unique(pair):
+                rows = np.sort(row[pair == p]).astype(np.int64)
+                sel[(int(p) // cfg.H, int(p) % cfg.H)] = rows
+    return sel
+
+
+def sample_rows_per_head(inp: PrefillInputs, rows_per_head: int):
+    """``rows_per_head`` seeded random query rows for every (b, h)."""
+    cfg = inp.cfg
+    sel = {}
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            rows = inp.rng.choice(cfg.Nq, size=min(rows_per_head, cfg.Nq), replace=False)
+            sel[(b, h)] = np.sort(rows).astype(np.int64)
+    return sel
+
+
+# ----------------------------------------------------------------------------------
+# Paged KV-cache decode workload
+# ----------------------------------------------------------------------------------
+@dataclasses.dataclass
+class DecodeInputs:
+    cfg: DecodeConfig
+    seq_lens: np.ndarray      # [S] int32, each sequence's cached length (current token included)
+    q: np.ndarray             # [S,H,d] uint16 bf16 bits
+    k_seq: list               # per sequence [L_s,Hkv,d] uint16 (contiguous, before paging)
+    v_seq: list
+    k_cache: np.ndarray       # [num_pages,page_size,Hkv,d] uint16
+    v_cache: np.ndarray
+    page_table: np.ndarray    # [S,max_pages_per_seq] int32
+    num_pages: int
+
+    @property
+    def max_pages_per_seq(self) -> int:
+        return int(self.page_table.shape[1])
+
+    def kv_bytes(self) -> int:
+        """K and V bytes the sequences own (the decode step must read all of them)."""
+        return int(self.seq_lens.astype(np.int64).sum()) * self.cfg.Hkv * self.cfg.d * 2 * 2
+
+
+def make_decode(cfg: DecodeConfig, seed: int | None = None, *, seq_lens=None,
+                unused_fill: str = "zero", table_pad: int = 0) -> DecodeInputs:
+    """Draw a paged KV cache.
+
+    Physical pages are a seeded permutation of 0..P_total-1 (P_total = sum of
+    ceil(L_s / page_size)), handed to the sequences in order. Slots of a page past a
+    sequence's length hold 0 (``unused_fill="zero"``) or bf16 NaN (``"nan"``); table
+    entries past a sequence's last page hold ``table_pad``.
+    ``seq_lens`` overrides the length draw (zero-length sequences are allowed).
+    """
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    S, P = cfg.num_seqs, cfg.page_size
+    if seq_lens is None:
+        lens = rng.integers(cfg.len_lo, cfg.len_hi, size=S, endpoint=True).astype(np.int32)
+    else:
+        lens = np.asarray(seq_lens, dtype=np.int32)
+        assert lens.shape == (S,)
+    n_pages = (lens.astype(np.int64) + P - 1) // P
+    total = int(n_pages.sum())
+    perm = rng.permutation(total).astype(np.int32)
+    max_pages = max(1, (cfg.max_seq_len + P - 1) // P)
+    assert int(lens.max(initial=0)) <= cfg.max_seq_len
+    table = np.full((S, max_pages), table_pad, dtype=np.int32)
+    off = 0
+    for s in range(S):
+        table[s, :n_pages[s]] = perm[off:off + n_pages[s]]
+        off += int(n_pages[s])
+
+    q = _draw(rng, (S, cfg.H, cfg.d), 1.0, "bf16")
+    fill = BF16_NAN_BITS if unused_fill == "nan" else np.uint16(0)
+    npool = max(total, 1)
+    k_cache = np.full((npool, P, cfg.Hkv, cfg.d), fill, dtype=np.uint16)
+    v_cache = np.full((npool, P, cfg.Hkv, cfg.d), fill, dtype=np.uint16)
+    k_seq, v_seq = [], []
+    for s in range(S):
+        L = int(lens[s])
+        ks = _draw(rng, (L, cfg.Hkv, cfg.d), 1.0, "bf16")
+        vs = _draw(rng, (L, cfg.Hkv, cfg.d), 1.0, "bf16")
+        t = np.arange(L)
+        pages = table[s, t // P]
+        k_cache[pages, t % P] = ks
+        v_cache[pages, t % P] = vs
+        k_seq.append(ks)
+        v_seq.append(vs)
+    return DecodeInputs(cfg, lens, q, k_seq, v_seq, k_cache, v_cache, table, npool)
+
+
+def custom_decode(num_seqs, H, Hkv, d, len_lo, len_hi, page_size=16, max_seq_len=None,
+                  scale=None, seed=0, **kw) -> DecodeInputs:
+    if max_seq_len is None:
+        max_seq_len = max(len_hi, 1)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    cfg = DecodeConfig("custom_decode", num_seqs, H, Hkv, d, len_lo, len_hi, page_size,
+                       max_seq_len, scale, seed)
+    return make_decode(cfg, **kw)

@@ -1,0 +1,103 @@
+"""Seeded input generation: bf16 rounding, determinism, paging layout (CPU only)."""
+import numpy as np
+import pytest
+
+from kv_cache_fa_amd import inputs
+
+
+def _f32(bits):
+    return np.array([bits], dtype=np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("bits,want", [
+    (0x3F800000, 0x3F80),   # 1.0 exact
+    (0x3F808000, 0x3F80),   # halfway, lower neighbour even -> round down
+    (0x3F818000, 0x3F82),   # halfway, lower neighbour odd  -> round up to even
+    (0x3F808001, 0x3F81),   # just above halfway -> up
+    (0x3F807FFF, 0x3F80),   # just below halfway -> down
+    (0xBF818000, 0xBF82),   # negative tie -> even (magnitude rounds up)
+    (0x00000000, 0x0000),
+    (0x80000000, 0x8000),   # -0 keeps its sign
+    (0x7F7FFFFF, 0x7F80),   # largest float rounds to +inf under RNE
+    (0x00008000, 0x0000),   # subnormal tie -> even (zero)
+])
+def test_bf16_round_to_nearest_even(bits, want):
+    got = inputs.f32_to_bf16_bits(_f32(bits))[0]
+    assert int(got) == want
+
+
+def test_bf16_widen_is_exact_roundtrip():
+    rng = np.random.default_rng(0)
+    b = inputs.f32_to_bf16_bits(rng.standard_normal(1000, dtype=np.float32))
+    assert np.array_equal(inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(b)), b)
+    x = inputs.bf16_bits_to_f32(b)
+    assert np.all(x.view(np.uint32) & 0xFFFF == 0)
+
+
+def test_prefill_is_deterministic_and_seeded():
+    cfg = inputs.PREFILL_CONFIGS["bf16_causal"]
+    small = inputs.PrefillConfig("t", 1, 2, 2, 16, 16, 64, True, "bf16", 0.5, 0.125, 2)
+    a, b = inputs.make_prefill(small), inputs.make_prefill(small)
+    assert a.q.dtype == np.uint16
+    assert np.array_equal(a.q, b.q) and np.array_equal(a.k, b.k) and np.array_equal(a.v, b.v)
+    c = inputs.make_prefill(small, seed=3)
+    assert not np.array_equal(a.q, c.q)
+    # draw order: Q first, from standard_normal(float32), times 0.5, then RNE
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((1, 2, 16, 64), dtype=np.float32) * np.float32(0.5)
+    assert np.array_equal(a.q, inputs.f32_to_bf16_bits(q))
+    assert cfg.flops == 4 * 64 * 2 * 8 * (1024 * 1025 // 2)
+
+
+def test_workload_flop_counts():
+    c = inputs.PREFILL_CONFIGS
+    assert c["gqa_causal"].flops == pytest.approx(549.9e9, rel=1e-3)
+    assert c["long_causal"].flops == pytest.approx(35.18e12, rel=1e-3)
+    assert c["fp32_single"].flops == 4 * 64 * 128 * 128
+    assert inputs.unmasked_pairs(3, 5, True) == 3 + 4 + 5
+    assert inputs.unmasked_pairs(4, 4, True) == 10
+
+
+def test_row_samples_are_seeded_and_distinct():
+    small = inputs.PrefillConfig("t", 2, 4, 2, 64, 64, 64, True, "bf16", 1.0, 0.125, 3)
+    a = inputs.sample_rows(inputs.make_prefill(small), 2, 50)
+    b = inputs.sample_rows(inputs.make_prefill(small), 2, 50)
+    assert a.keys() == b.keys()
+    assert all(np.array_equal(a[x], b[x]) for x in a)
+    full = [x for x in a if len(a[x]) == 64]
+    assert len(full) == 2
+    assert sum(len(r) for x, r in a.items() if x not in full) == 50
+
+
+def test_decode_layout():
+    inp = inputs.custom_decode(6, 8, 2, 32, 1, 70, page_size=16, max_seq_len=80, seed=5)
+    assert inp.page_table.shape == (6, 5)
+    assert inp.page_table.dtype == np.int32 and inp.seq_lens.dtype == np.int32
+    assert np.all((inp.seq_lens >= 1) & (inp.seq_lens <= 70))
+    n_pages = (inp.seq_lens + 15) // 16
+    assert inp.num_pages == int(n_pages.sum())
+    for s in range(6):
+        L = int(inp.seq_lens[s])
+        # unused table entries hold the pad value, unused slots hold the fill value
+        assert np.all(inp.page_table[s, n_pages[s]:] == 0)
+        last = inp.page_table[s, n_pages[s] - 1]
+        tail = L - (n_pages[s] - 1) * 16
+        assert np.all(inp.k_cache[last, tail:] == 0)
+    nan = inputs.custom_decode(2, 4, 1, 8, 5, 5, max_seq_len=16, seed=1, unused_fill="nan",
+                               table_pad=-1)
+    assert np.all(nan.k_cache[nan.page_table[0, 0], 5:] == inputs.BF16_NAN_BITS)
+    assert np.all(nan.page_table[:, 1:] == -1)
+
+
+def test_decode_zero_length_sequences():
+    cfg = inputs.DecodeConfig("z", 3, 4, 2, 8, 0, 0, 16, 32, 0.35, 0)
+    inp = inputs.make_decode(cfg, seq_lens=[0, 17, 0])
+    assert inp.num_pages == 2
+    assert inp.k_seq[0].shape == (0, 2, 8)
+
+
+def test_paged_decode_config_lengths():
+    cfg = inputs.DECODE_CONFIGS["paged_decode"]
+    rng = np.random.default_rng(cfg.seed)
+    lens = rng.integers(cfg.len_lo, cfg.len_hi, size=cfg.num_seqs, endpoint=True)
+    assert lens.min() >= 512 and lens.max() <= 8192

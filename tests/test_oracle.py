@@ -1,0 +1,194 @@
+"""The fp64 oracle checked against what the pages and the mathematics fix (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_fa_amd import inputs
+from pins import ALL_PINS, load_golden, parse_arr, parse_num
+
+
+def dense_attn(q, k, v, causal, scale):
+    return oracle.attention(q, k, v, causal=causal, scale=scale)
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(dense_attn)
+
+
+def test_rows_mode_matches_dense():
+    rng = np.random.default_rng(1)
+    q, k, v = (rng.standard_normal(s) for s in [(2, 4, 9, 8), (2, 2, 9, 8), (2, 2, 9, 8)])
+    O, L = oracle.attention(q, k, v, causal=True, scale=0.3)
+    rows = {(1, 3): np.array([0, 4, 8]), (0, 0): np.arange(9)}
+    Or, Lr = oracle.attention(q, k, v, causal=True, scale=0.3, rows=rows)
+    for (b, h), idx in rows.items():
+        np.testing.assert_array_equal(Or[(b, h)], O[b, h, idx])
+        np.testing.assert_array_equal(Lr[(b, h)], L[b, h, idx])
+
+
+def test_probability_rows_sum_to_one_and_respect_mask():
+    """Each softmax row is a probability distribution over the allowed keys."""
+    rng = np.random.default_rng(2)
+    q, k, v = (rng.standard_normal(s) * 3 for s in [(1, 2, 7, 4), (1, 1, 11, 4), (1, 1, 11, 4)])
+    for causal in (False, True):
+        _, _, P = oracle.attention(q, k, v, causal=causal, scale=1.0, return_probs=True)
+        mask = oracle.allowed_keys(7, 11, causal)
+        for p in P.values():
+            np.testing.assert_allclose(p.sum(-1), 1.0, rtol=0, atol=1e-13)
+            assert np.all(p[~mask] == 0.0)
+            assert np.all(p[mask] > 0.0)
+
+
+def test_softmax_shift_of_score_rows():
+    """softmax(x) = softmax(x - c): adding a per-row constant leaves P unchanged."""
+    rng = np.random.default_rng(3)
+    s = rng.standard_normal((5, 9)) * 4
+    c = rng.standard_normal((5, 1)) * 50
+    mask = np.ones_like(s, dtype=bool)
+    P1, m1, l1 = oracle.softmax_rows(s, mask)
+    P2, m2, l2 = oracle.softmax_rows(s + c, mask)
+    np.testing.assert_allclose(P2, P1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, rtol=1e-13)
+    np.testing.assert_allclose(m2, m1 + c[:, 0], rtol=0, atol=1e-12)
+
+
+# ---- online softmax (the pages' recurrence) and the log-sum-exp merge ------------
+def test_online_softmax_golden_steps():
+    g = load_golden("online_softmax.json")
+    for ex in g["stats"]:
+        scores = [parse_num(x) for x in ex["scores"]]
+        trace = []
+        M, L = oracle.online_softmax_stats(scores, ex["blocks"], trace=trace)
+        assert len(trace) == len(ex["steps"])
+        for got, want in zip(trace, ex["steps"]):
+            for key in ("m_new", "l_block", "M", "L"):
+                assert got[key] == pytest.approx(parse_num(want[key]), abs=1e-14), key
+            if "L_old_rescaled" in want:
+                assert got["L_old_rescaled"] == pytest.approx(want["L_old_rescaled"], abs=1e-14)
+        assert M == pytest.approx(parse_num(ex["M"]), abs=1e-14)
+        assert L == pytest.approx(ex["L"], abs=1e-14)
+
+
+def test_merge_golden():
+    m = load_golden("online_softmax.json")["merge"]
+    O, LSE = oracle.merge_partials(parse_arr(m["o_parts"]), parse_arr(m["lse_parts"]))
+    np.testing.assert_allclose(O, parse_arr(m["O"]), rtol=0, atol=1e-13)
+    assert LSE == pytest.approx(parse_num(m["LSE"]), abs=1e-14)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_online_recurrence_equals_definition(seed):
+    """Any blocking of the row gives the whole-row softmax statistics and output."""
+    rng = np.random.default_rng(100 + seed)
+    N, d = 37, 6
+    s = rng.standard_normal(N) * 5
+    v = rng.standard_normal((N, d))
+    cuts = np.sort(rng.choice(np.arange(1, N), size=rng.integers(1, 8), replace=False))
+    blocks = np.diff(np.concatenate([[0], cuts, [N]])).tolist()
+    M, L = oracle.online_softmax_stats(s, blocks)
+    P, m, l = oracle.softmax_rows(s[None], np.ones((1, N), dtype=bool))
+    assert M == m[0]
+    assert L == pytest.approx(l[0], rel=1e-13)
+    o, lse = oracle.online_attention_row(s, v, blocks)
+    np.testing.assert_allclose(o, P[0] @ v, rtol=0, atol=1e-12)
+    assert lse == pytest.approx(m[0] + math.log(l[0]), abs=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_merge_of_splits_equals_whole(seed):
+    """Attention over disjoint key sets, merged by log-sum-exp, equals the whole row;
+    empty parts (LSE = -inf) weigh nothing."""
+    rng = np.random.default_rng(200 + seed)
+    Nk, d = 50, 8
+    q = rng.standard_normal((1, 1, 1, d)) * 2
+    k = rng.standard_normal((1, 1, Nk, d))
+    v = rng.standard_normal((1, 1, Nk, d))
+    O, L = oracle.attention(q, k, v, causal=False, scale=0.5)
+    cuts = np.sort(rng.choice(np.arange(1, Nk), size=4, replace=False))
+    parts = np.split(np.arange(Nk), cuts)
+    os_, ls_ = [], []
+    for idx in parts:
+        o, l = oracle.attention(q, k[:, :, idx], v[:, :, idx], causal=False, scale=0.5)
+        os_.append(o[0, 0, 0])
+        ls_.append(l[0, 0, 0])
+    os_.append(np.full(d, 123.0))      # an empty split: its output must not matter
+    ls_.append(-np.inf)
+    Om, Lm = oracle.merge_partials(os_, ls_)
+    np.testing.assert_allclose(Om, O[0, 0, 0], rtol=0, atol=1e-12)
+    assert Lm == pytest.approx(L[0, 0, 0], abs=1e-12)
+
+
+def test_merge_all_empty():
+    O, L = oracle.merge_partials(np.zeros((3, 4)), [-np.inf] * 3)
+    assert L == -np.inf and np.all(O == 0)
+
+
+# ---- decode against a paged cache ----------------------------------------------
+def test_decode_equals_last_row_of_causal_prefill():
+    """The decode query is the newest token: its result is the last row of a causal
+    prefill over the same keys (glossary entry 'KV Cache')."""
+    rng = np.random.default_rng(4)
+    S, H, Hkv, d = 3, 8, 2, 16
+    lens = [1, 7, 40]
+    ks = [rng.standard_normal((L, Hkv, d)) for L in lens]
+    vs = [rng.standard_normal((L, Hkv, d)) for L in lens]
+    q = rng.standard_normal((S, H, d))
+    O, LSE = oracle.decode(q, ks, vs, scale=0.25)
+    for s, L in enumerate(lens):
+        qq = np.zeros((1, H, L, d))
+        qq[0, :, -1] = q[s]
+        kk = ks[s].transpose(1, 0, 2)[None]
+        vv = vs[s].transpose(1, 0, 2)[None]
+        Op, Lp = oracle.attention(qq, kk, vv, causal=True, scale=0.25)
+        np.testing.assert_allclose(O[s], Op[0, :, -1], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(LSE[s], Lp[0, :, -1], rtol=0, atol=1e-13)
+
+
+def test_decode_empty_sequence():
+    q = np.ones((2, 4, 8))
+    ks = [np.zeros((0, 2, 8)), np.ones((3, 2, 8))]
+    O, LSE = oracle.decode(q, ks, ks, scale=1.0)
+    assert np.all(O[0] == 0) and np.all(LSE[0] == -np.inf)
+    np.testing.assert_allclose(O[1], 1.0)
+    np.testing.assert_allclose(LSE[1], 8.0 + math.log(3))
+
+
+def test_gather_pages_is_bit_exact_and_table_is_a_permutation():
+    inp = inputs.custom_decode(5, 8, 2, 16, 1, 100, page_size=16, max_seq_len=100, seed=7)
+    n_pages = (inp.seq_lens + 15) // 16
+    used = np.concatenate([inp.page_table[s, :n_pages[s]] for s in range(5)])
+    assert np.array_equal(np.sort(used), np.arange(int(n_pages.sum())))
+    for cache, seqs in ((inp.k_cache, inp.k_seq), (inp.v_cache, inp.v_seq)):
+        got = oracle.gather_pages(cache, inp.page_table, inp.seq_lens, 16)
+        for a, b in zip(got, seqs):
+            assert a.dtype == b.dtype == np.uint16
+            assert np.array_equal(a, b)
+
+
+def test_gather_pages_detects_a_wrong_slot():
+    """A one-token shift of the slot index is caught bit-exactly."""
+    inp = inputs.custom_decode(2, 4, 1, 8, 20, 40, page_size=16, max_seq_len=40, seed=8)
+    s, L = 0, int(inp.seq_lens[0])
+    t = np.arange(L)
+    wrong = inp.k_cache[inp.page_table[s, t // 16], (t + 1) % 16]
+    assert not np.array_equal(wrong, inp.k_seq[s])
+
+
+def test_size_facts_from_the_pages():
+    """The pages' printed sizes agree with the counting used for measurement."""
+    facts = load_golden("size_facts.json")["facts"]
+    n128k, n8k, kv = facts
+    assert n128k["tokens"] ** 2 == n128k["value"]
+    assert abs(n128k["value"] - 16.4e9) / 16.4e9 <= n128k["rel_tol"]
+    assert n8k["tokens"] ** 2 == n8k["value"]
+    assert abs(n8k["value"] - 67e6) / 67e6 <= n8k["rel_tol"]
+    b = 2 * kv["layers"] * kv["kv_heads"] * kv["head_dim"] * kv["tokens"] * kv["bytes_per_value"]
+    assert b == kv["value"]
+    assert abs(b - 500e6) / 500e6 <= kv["rel_tol"]
+    # one layer of the decode workload's K+V for a sequence of L tokens, as counted by
+    # DecodeInputs.kv_bytes: 2 (K,V) x Hkv x d x L x 2 bytes
+    inp = inputs.custom_decode(3, 8, 8, 128, 4096, 4096, max_seq_len=4096, seed=0)
+    assert inp.kv_bytes() * kv["layers"] == 3 * kv["value"]
