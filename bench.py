@@ -1,0 +1,300 @@
+"""Throughput of the exact-attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--prefill long_causal|gqa_causal]
+                    [--no-cpu-baseline] [--no-extra] [--calibrate-copy]
+
+One step = one pass over every stage of the path on one batch of synthetic,
+seeded input already resident in HBM:
+  * causal bf16 prefill, fa_fwd (default: B1 H8 N131072 d128, the long-context
+    workload), and
+  * paged-KV decode, fa_decode_paged (64 sequences x 1 query, H32 Hkv8 d128,
+    lengths U{512..8192}, 16-token pages; split-K kernel + log-sum-exp combine).
+W untimed steps, then K timed steps bracketed by device synchronisation. Prints one
+JSON line. Every launch goes through the C ABI of libkvfa.so on torch's current
+stream; HIP events on that stream time each call.
+
+Only the cpu_baseline leg touches the fp64 oracle (timed on a bounded sample).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from kv_cache_fa_amd import _lib, inputs  # noqa: E402
+
+METRIC = "prefill attn TFLOP/s (bf16 causal) + decode KV GB/s, % of MI355X peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = {
+    "fwd_bf16_kernel": os.path.join(ROOT, "kv_cache_fa_amd", "csrc", "prefill_bf16.hip"),
+    "decode_split_kernel": os.path.join(ROOT, "kv_cache_fa_amd", "csrc", "decode.hip"),
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter runs, if they still describe
+    the current kernel source (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("workload") != workload:
+        return None
+    if rec.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def decode_bytes(inp: inputs.DecodeInputs) -> int:
+    """Algorithmic bytes of one decode call: the K/V the sequences own, Q, O, lse,
+    the page-table entries read and seq_lens (the split-K workspace is not counted)."""
+    c = inp.cfg
+    n_pages = int(((inp.seq_lens.astype(np.int64) + c.page_size - 1) // c.page_size).sum())
+    return (inp.kv_bytes() + 2 * c.num_seqs * c.H * c.d * 2 + c.num_seqs * c.H * 4
+            + n_pages * 4 + c.num_seqs * 4)
+
+
+def decode_flops(inp: inputs.DecodeInputs) -> float:
+    return 4.0 * inp.cfg.d * inp.cfg.H * float(inp.seq_lens.astype(np.int64).sum())
+
+
+def cpu_baseline(pinp: inputs.PrefillInputs, budget_s: float = 12.0):
+    """The fp64 oracle (as it stands) on a bounded sample of the prefill workload:
+    random query rows of head 0, each against its full causal prefix."""
+    import oracle  # test infrastructure, used only for this baseline leg
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()
+                     if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    c = pinp.cfg
+    q = inputs.bf16_bits_to_f64(pinp.q[:1, :1])
+    k = inputs.bf16_bits_to_f64(pinp.k[:1, :1])
+    v = inputs.bf16_bits_to_f64(pinp.v[:1, :1])
+    rng = np.random.default_rng(1234)
+    done_rows, flops, t_used = 0, 0.0, 0.0
+    batch = 32
+    while t_used < budget_s:
+        rows = np.sort(rng.choice(c.Nq, size=batch, replace=False))
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, causal=c.causal, scale=c.scale, rows={(0, 0): rows})
+        t_used += time.perf_counter() - t0
+        n_keys = (rows + (c.Nk - c.Nq) + 1) if c.causal else np.full(batch, c.Nk)
+        flops += 4.0 * c.d * float(n_keys.sum())
+        done_rows += batch
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done_rows} random query rows of head 0 of {c.name} (each over its "
+                      f"full causal prefix), fp64 NumPy, {t_used:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--prefill", default="long_causal", choices=["long_causal", "gqa_causal"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the separately timed GQA prefill measurement")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    _lib.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- inputs (seeded, synthetic), resident in HBM before timing ----
+    pcfg = inputs.PREFILL_CONFIGS[args.prefill]
+    log(f"[bench] generating {pcfg.name} inputs")
+    pinp = inputs.make_prefill(pcfg)
+    pq, pk, pv = to_dev(pinp.q), to_dev(pinp.k), to_dev(pinp.v)
+    po = torch.empty_like(pq)
+    plse = torch.empty((pcfg.B, pcfg.H, pcfg.Nq), dtype=torch.float32, device=dev)
+
+    dcfg = inputs.DECODE_CONFIGS["paged_decode"]
+    log("[bench] generating paged_decode inputs")
+    dinp = inputs.make_decode(dcfg)
+    dq, dkc, dvc = to_dev(dinp.q), to_dev(dinp.k_cache), to_dev(dinp.v_cache)
+    dpt = torch.from_numpy(dinp.page_table).to(dev)
+    dsl = torch.from_numpy(dinp.seq_lens).to(dev)
+    do = torch.empty_like(dq)
+    dlse = torch.empty((dcfg.num_seqs, dcfg.H), dtype=torch.float32, device=dev)
+    ws = torch.empty(_lib.fa_decode_paged_workspace_size(dcfg.num_seqs, dcfg.H, dcfg.Hkv,
+                                                         dcfg.d, dcfg.max_seq_len), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+
+    def prefill():
+        _lib.fa_fwd(pq, pk, pv, po, plse, causal=pcfg.causal, scale=pcfg.scale, stream=stream)
+
+    def decode():
+        _lib.fa_decode_paged(dq, dkc, dvc, dpt, dsl, do, dlse, max_seq_len=dcfg.max_seq_len,
+                             scale=dcfg.scale, workspace=ws, stream=stream)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {K} steps")
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        prefill()
+        ev[i][1].record(stream)
+        ev[i][2].record(stream)
+        decode()
+        ev[i][3].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    step_ms = start.elapsed_time(end) / K
+    p_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    d_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+
+    p_flops = pcfg.flops
+    d_bytes = decode_bytes(dinp)
+    d_flops = decode_flops(dinp)
+    value = (p_flops + d_flops) / (step_ms * 1e-3) / 1e12
+    p_tflops = p_flops / (p_ms.mean() * 1e-3) / 1e12
+    d_gbs = d_bytes / (d_ms.mean() * 1e-3) / 1e9
+
+    p_traffic = measured_traffic("fwd_bf16_kernel", pcfg.name)
+    d_traffic = measured_traffic("decode_split_kernel", dcfg.name)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16; paged cache with seeded page permutation)",
+        "config": {
+            "workload": f"{pcfg.name} prefill + paged_decode",
+            "prefill": {"B": pcfg.B, "H": pcfg.H, "Hkv": pcfg.Hkv, "N": pcfg.Nq, "d": pcfg.d,
+                        "causal": pcfg.causal, "flops": p_flops},
+            "decode": {"num_seqs": dcfg.num_seqs, "H": dcfg.H, "Hkv": dcfg.Hkv, "d": dcfg.d,
+                       "seq_len": f"U{{{dcfg.len_lo}..{dcfg.len_hi}}}",
+                       "total_kv_tokens": int(dinp.seq_lens.sum()), "page_size": dcfg.page_size,
+                       "bytes": d_bytes},
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "fwd_bf16_kernel",
+            "bound": "mfma",
+            "achieved": round(p_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": p_traffic,
+        },
+        "legs": {
+            "prefill": {"ms_mean": round(float(p_ms.mean()), 4),
+                        "ms_p10": round(float(np.percentile(p_ms, 10)), 4),
+                        "ms_p90": round(float(np.percentile(p_ms, 90)), 4),
+                        "TFLOP/s": round(p_tflops, 2),
+                        "frac_of_bf16_peak": round(p_tflops / PEAK_BF16_TFLOPS, 4)},
+            "decode": {"ms_mean": round(float(d_ms.mean()), 4),
+                       "ms_p10": round(float(np.percentile(d_ms, 10)), 4),
+                       "ms_p90": round(float(np.percentile(d_ms, 90)), 4),
+                       "GB/s": round(d_gbs, 1),
+                       "frac_of_hbm_peak": round(d_gbs / PEAK_HBM_GBS, 4),
+                       "roofline": {"kernel": "decode_split_kernel + decode_combine_kernel",
+                                    "bound": "hbm", "achieved": round(d_gbs, 1),
+                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": round(d_gbs / PEAK_HBM_GBS, 4),
+                                    "traffic": d_traffic}},
+        },
+        "wall_s_timed": round(t_wall, 3),
+    }
+
+    if not args.no_extra and args.prefill != "gqa_causal":
+        gcfg = inputs.PREFILL_CONFIGS["gqa_causal"]
+        log("[bench] extra: gqa_causal prefill")
+        ginp = inputs.make_prefill(gcfg)
+        gq, gk, gv = to_dev(ginp.q), to_dev(ginp.k), to_dev(ginp.v)
+        go = torch.empty_like(gq)
+        glse = torch.empty((gcfg.B, gcfg.H, gcfg.Nq), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            _lib.fa_fwd(gq, gk, gv, go, glse, causal=True, scale=gcfg.scale, stream=stream)
+        n = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            _lib.fa_fwd(gq, gk, gv, go, glse, causal=True, scale=gcfg.scale, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        g_ms = e0.elapsed_time(e1) / n
+        g_tf = gcfg.flops / (g_ms * 1e-3) / 1e12
+        out["legs"]["prefill_gqa_causal"] = {
+            "B": gcfg.B, "H": gcfg.H, "Hkv": gcfg.Hkv, "N": gcfg.Nq, "d": gcfg.d,
+            "ms_mean": round(g_ms, 4), "TFLOP/s": round(g_tf, 2),
+            "frac_of_bf16_peak": round(g_tf / PEAK_BF16_TFLOPS, 4)}
+        del gq, gk, gv, go, glse
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        out["calibration_copy_bytes"] = n
+
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle sample)")
+        out["cpu_baseline"] = cpu_baseline(pinp)
+
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,118 @@
+/*
+ * kvfa.h — C ABI of the exact-attention library (libkvfa.so) for AMD MI355X (gfx950).
+ *
+ * The library computes exact attention, O = softmax(scale * Q K^T) V with row-wise
+ * softmax, as defined on the page "Donanıma Duyarlı Algoritma Tasarımı:
+ * FlashAttention" (section "Transformer Mimarisi ve Self-Attention Mekanizması"),
+ * the FlashAttention way: Q, K and V are processed in tiles held on chip and a
+ * running row maximum and row sum ("Online Softmax Prensibi", steps 1-5) replace the
+ * materialised score matrix. Besides O it returns the per-row softmax statistics
+ * that page keeps in HBM (section "FlashAttention-1 (İki Geçişli Yaklaşım)") as one
+ * natural-log log-sum-exp per row: lse = M + ln L.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named as tensors are DEVICE pointers, allocated and owned by the caller.
+ *   The library never allocates or frees device memory and keeps no global mutable
+ *   state; calls on different streams are independent.
+ * - Every tensor is dense and row-major with the head dimension d innermost; there
+ *   are no stride arguments. bf16 tensors are passed as raw 16-bit patterns.
+ * - Tensor pointers must be 16-byte aligned. lse may be NULL (then it is not written).
+ * - stream is a hipStream_t (NULL = the default stream). Work is only enqueued: a
+ *   return of FA_OK means "launched", device-side results are ready after the
+ *   caller synchronises the stream.
+ * - Errors: invalid arguments return FA_ERR_INVALID or FA_ERR_UNSUPPORTED before
+ *   anything is enqueued (no output is touched); a failed launch returns
+ *   FA_ERR_HIP. Nothing crosses the ABI as an exception.
+ * - Causal masking is bottom-right aligned: query i sits at absolute position
+ *   Nk - Nq + i and attends keys j <= i + (Nk - Nq) (new queries come after the
+ *   cached keys, as in the KV-cache flow of the glossary entry "KV Cache
+ *   (Anahtar-Değer Önbelleği)", yapayzekasozluk.tr/etiket/attention).
+ * - Grouped-query attention (same glossary entry: several query heads share one
+ *   K-V head): query head h reads K/V head h / (H / Hkv); H % Hkv must be 0.
+ */
+#ifndef KVFA_H
+#define KVFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID = -1,      /* an argument is out of its documented range           */
+    FA_ERR_UNSUPPORTED = -2,  /* a valid request this build does not implement        */
+    FA_ERR_HIP = -3           /* the HIP runtime reported an error at launch          */
+} fa_status;
+
+/*
+ * fa_fwd — bf16 prefill attention, fp32 accumulation.
+ *   q   [B, H,   Nq, d] bf16        o   [B, H, Nq, d] bf16 (written)
+ *   k   [B, Hkv, Nk, d] bf16        lse [B, H, Nq]    fp32 (written; may be NULL)
+ *   v   [B, Hkv, Nk, d] bf16
+ * d must be 64 or 128 (else FA_ERR_UNSUPPORTED). B, H, Hkv, Nq, Nk >= 1;
+ * causal requires Nq <= Nk; scale must be finite and > 0 (normally 1/sqrt(d));
+ * Nk * d * 2 and Nq * d * 2 must each be below 2^31 bytes (one head's slice).
+ * Scores, the softmax and the accumulator are fp32; P and O are rounded to bf16
+ * with round-to-nearest-even.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+           void* stream);
+
+/*
+ * fa_fwd_fp32 — the same operation with fp32 inputs and outputs and fp32 arithmetic
+ * throughout (no reduced-precision step). Same layouts, ranges and errors as fa_fwd.
+ */
+int fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse,
+                int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                void* stream);
+
+/*
+ * fa_decode_paged — one new query token per sequence against a paged KV cache
+ * (glossary entry "KV Cache (Anahtar-Değer Önbelleği)": token n+1 reads the cached
+ * K/V of the tokens before it; the cache is kept in fixed-size pages).
+ *   q          [num_seqs, H, d] bf16
+ *   k_cache    [num_pages, page_size, Hkv, d] bf16; token t of sequence s is slot
+ *   v_cache     t % page_size of physical page page_table[s][t / page_size]
+ *   page_table [num_seqs, max_pages_per_seq] int32
+ *   seq_lens   [num_seqs] int32, device memory: cached tokens per sequence, the
+ *              current token's K/V already appended (the query attends all of them)
+ *   o          [num_seqs, H, d] bf16 (written)   lse [num_seqs, H] fp32 (may be NULL)
+ *   workspace  device scratch of at least fa_decode_paged_workspace_size(...) bytes,
+ *              owned by the caller; its contents on entry do not matter.
+ * Work is split over the KV length (split-K); the partial results are merged by their
+ * log-sum-exps in a second kernel on the same stream.
+ * Requirements: page_size == 16 and d in {64, 128} (else FA_ERR_UNSUPPORTED);
+ * H % Hkv == 0 and H / Hkv <= 16, or a multiple of 16; num_seqs, H, Hkv,
+ * num_pages >= 1; max_pages_per_seq * page_size >= max_seq_len >= 1.
+ * Device-side values: a seq_len outside [0, max_seq_len] is clamped into it; a
+ * sequence with seq_len 0 gets O = 0 and lse = -inf; page ids outside
+ * [0, num_pages) are never dereferenced (their tokens are skipped, so the result is
+ * then not meaningful). Table entries past a sequence's last page and page slots
+ * past its length are never read.
+ */
+size_t fa_decode_paged_workspace_size(int num_seqs, int H, int Hkv, int d,
+                                      int max_seq_len, int page_size);
+
+int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* page_table, const int32_t* seq_lens, int page_size,
+                    void* o, float* lse, int num_seqs, int H, int Hkv, int d,
+                    int num_pages, int max_pages_per_seq, int max_seq_len, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Tokens of KV one split-K work-group covers for these sizes (a multiple of the page
+ * size); the workspace holds ceil(max_seq_len / split) partial results per head. */
+int fa_decode_paged_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVFA_H */

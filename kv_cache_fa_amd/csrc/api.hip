@@ -1,0 +1,112 @@
+// C ABI of libkvfa.so (declared in include/kvfa.h): argument validation and dispatch.
+// Validation runs entirely on the host and returns before any HIP call, so a rejected
+// call enqueues nothing and touches no output.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/kvfa.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shared checks of the two prefill entry points.
+int check_prefill(const void* q, const void* k, const void* v, const void* o, const void* lse,
+                  int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                  size_t elem) {
+    if (!q || !k || !v || !o) return FA_ERR_INVALID;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+        return FA_ERR_INVALID;
+    if (lse && !aligned(lse, 4)) return FA_ERR_INVALID;
+    if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return FA_ERR_INVALID;
+    if (H % Hkv != 0) return FA_ERR_INVALID;
+    if (causal && Nq > Nk) return FA_ERR_INVALID;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    // One head's slice is addressed with 32-bit byte offsets.
+    const unsigned long long lim = 1ull << 31;
+    if ((unsigned long long)Nk * d * elem >= lim || (unsigned long long)Nq * d * elem >= lim)
+        return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+           int Hkv, int Nq, int Nk, int d, int causal, float scale, void* stream) {
+    int st = check_prefill(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale, 2);
+    if (st != FA_OK) return st;
+    const unsigned long long n_wg = (unsigned long long)((Nq + 127) / 128) * B * H;
+    if (n_wg >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+    hipError_t e = kvfa::launch_fwd_bf16(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal != 0, scale,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
+                int H, int Hkv, int Nq, int Nk, int d, int causal, float scale, void* stream) {
+    int st = check_prefill(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale, 4);
+    if (st != FA_OK) return st;
+    if (H > 65535 || B > 65535) return FA_ERR_UNSUPPORTED;
+    hipError_t e = kvfa::launch_fwd_fp32(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal != 0, scale,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_decode_paged_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size) {
+    if (num_seqs < 1 || Hkv < 1 || max_seq_len < 1 || page_size != 16) return 0;
+    return kvfa::decode_split_tokens(num_seqs, Hkv, max_seq_len, page_size);
+}
+
+size_t fa_decode_paged_workspace_size(int num_seqs, int H, int Hkv, int d, int max_seq_len,
+                                      int page_size) {
+    if (num_seqs < 1 || H < 1 || Hkv < 1 || max_seq_len < 1 || page_size != 16) return 0;
+    if (d != 64 && d != 128) return 0;
+    return kvfa::decode_workspace_bytes(num_seqs, H, Hkv, d, max_seq_len, page_size);
+}
+
+int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* page_table, const int32_t* seq_lens, int page_size, void* o,
+                    float* lse, int num_seqs, int H, int Hkv, int d, int num_pages,
+                    int max_pages_per_seq, int max_seq_len, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !o || !workspace)
+        return FA_ERR_INVALID;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+        !aligned(workspace, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4))
+        return FA_ERR_INVALID;
+    if (lse && !aligned(lse, 4)) return FA_ERR_INVALID;
+    if (num_seqs < 1 || H < 1 || Hkv < 1 || num_pages < 1 || max_pages_per_seq < 1 ||
+        max_seq_len < 1)
+        return FA_ERR_INVALID;
+    if (H % Hkv != 0) return FA_ERR_INVALID;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID;
+    if (page_size != 16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+    if ((long long)max_pages_per_seq * page_size < max_seq_len) return FA_ERR_INVALID;
+    const int g = H / Hkv;
+    if (g > 16 && g % 16 != 0) return FA_ERR_UNSUPPORTED;
+    if (num_seqs > 65535 || (long long)Hkv * (g > 16 ? g / 16 : 1) > 65535)
+        return FA_ERR_UNSUPPORTED;
+    if (workspace_bytes < kvfa::decode_workspace_bytes(num_seqs, H, Hkv, d, max_seq_len, page_size))
+        return FA_ERR_INVALID;
+    hipError_t e = kvfa::launch_decode_paged(q, k_cache, v_cache, page_table, seq_lens, o, lse,
+                                             num_seqs, H, Hkv, d, num_pages, max_pages_per_seq,
+                                             max_seq_len, scale, workspace,
+                                             static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID: return "FA_ERR_INVALID: an argument is out of its documented range";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: valid request not implemented";
+        case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
+        default: return "unknown fa_status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,338 @@
+// Single-token decode against a paged KV cache: split-K attention + log-sum-exp merge.
+//
+// Method: glossary entry "KV Cache (Anahtar-Değer Önbelleği)" (yapayzekasozluk.tr,
+// tag "Attention"): the new token's query reads the cached K/V of every earlier token
+// (its own K/V already appended); the cache lives in fixed-size pages; under GQA
+// several query heads share one K/V head. The softmax over the cached keys uses the
+// running max / running sum merge of page "Donanıma Duyarlı Algoritma Tasarımı:
+// FlashAttention", "Online Softmax Prensibi" steps 1-5, both inside a split (page by
+// page) and across splits (the combine kernel merges (O_k, lse_k) pairs, the same
+// algebra expressed through one log-sum-exp per part).
+//
+// gfx950 mapping (this design):
+// * Work-group = (sequence, KV head, split of `split_tokens` keys), 4 waves; wave w
+//   takes pages w, w+4, ... of its split. All query heads of the GQA group are
+//   served from one read of each K/V page, so every cached byte is read once.
+// * Scores: S^T[token][head] = K_page Q^T with v_mfma_f32_16x16x32_bf16 — one page
+//   (16 tokens) is exactly the MFMA's 16 rows, the group's heads fill its columns.
+//   K rows go straight from HBM into the A operand (no LDS).
+// * P.V: plain FMAs. A lane owns one 16-byte chunk of V rows (8 dims) for a subset of
+//   the page's tokens and accumulates all heads of the group; the probabilities reach
+//   it through a small per-wave LDS table.
+// * The split's partial result (normalised O_k, lse_k in log2 units) goes to the
+//   caller's workspace; a second kernel merges the splits in order.
+#include "common.h"
+#include "launch.h"
+
+namespace kvfa {
+
+namespace {
+
+constexpr int kPage = 16;
+constexpr int kWaves = 4;
+
+template <int D, int GH>
+__global__ __launch_bounds__(256) void decode_split_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kcache,
+    const uint16_t* __restrict__ vcache, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
+    float* __restrict__ lse_part, int H, int Hkv, int g, int n_hg, int num_pages,
+    int max_pages, int max_seq_len, int split_tokens, int max_splits, float scale_log2,
+    float tau_raw) {
+    constexpr int CH = D / 8;          // 16-byte chunks per token row
+    constexpr int TG = 64 / CH;        // token groups of the P.V lane layout
+    constexpr int TPL = kPage / TG;    // tokens per lane in P.V
+    constexpr int KS = D / 32;         // MFMA k-steps over the head dimension
+    __shared__ float p_lds[kWaves][kPage][GH];
+    __shared__ float a_lds[kWaves][GH];
+    __shared__ float red_m[kWaves][GH];
+    __shared__ float red_l[kWaves][GH];
+    __shared__ float red_o[kWaves][GH][D];
+
+    const int s = blockIdx.z;
+    const int kvh = blockIdx.y / n_hg, hg = blockIdx.y % n_hg;
+    const int split = blockIdx.x;
+    const int L = min(max(seq_lens[s], 0), max_seq_len);
+    const int t0 = split * split_tokens;
+    if (t0 >= L) return;  // uniform: this split holds no cached token
+    const int t1 = min(t0 + split_tokens, L);
+    const int first_page = t0 / kPage;
+    const int n_pg = (t1 - t0 + kPage - 1) / kPage;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n = lane & 15;     // head column of S^T held by this lane
+    const int kq = lane >> 4;    // k-slot group / token quad of S^T
+    const int tg = lane / CH, c = lane % CH;  // P.V layout: token group, V chunk
+    const int h0 = kvh * g + hg * GH;
+    const int nheads = min(GH, g - hg * GH);
+    const size_t tok_stride = (size_t)Hkv * D;  // elements between consecutive slots
+
+    // B operand (Q^T): Q[s][h0+n][8*(4j + kq) .. +7], zero for padding columns.
+    u32x4 qf[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+        qf[j] = u32x4{0, 0, 0, 0};
+        if (n < nheads)
+            qf[j] = *reinterpret_cast<const u32x4*>(q + ((size_t)s * H + h0 + n) * D +
+                                                     (j * 4 + kq) * 8);
+    }
+
+    float m_used = -INFINITY, l_part = 0.f;
+    float oacc[GH][8];
+#pragma unroll
+    for (int hh = 0; hh < GH; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oacc[hh][e] = 0.f;
+
+    for (int pi = w; pi < n_pg; pi += kWaves) {
+        const int pidx = first_page + pi;
+        const int pid = __builtin_amdgcn_readfirstlane(page_table[(size_t)s * max_pages + pidx]);
+        if ((unsigned)pid >= (unsigned)num_pages) continue;  // never dereference a bad id
+        const size_t page_base = (size_t)pid * kPage * tok_stride + (size_t)kvh * D;
+        const int tok0 = pidx * kPage;
+
+        u32x4 kf[KS], vv[TPL];
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+            kf[j] = *reinterpret_cast<const u32x4*>(kcache + page_base + n * tok_stride +
+                                                     (j * 4 + kq) * 8);
+#pragma unroll
+        for (int i = 0; i < TPL; ++i)
+            vv[i] = *reinterpret_cast<const u32x4*>(vcache + page_base +
+                                                     (tg + TG * i) * tok_stride + c * 8);
+
+        // S^T: acc[i] = score of token 4*kq + i for head column n
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KS; ++j) acc = mfma16x16x32(kf[j], qf[j], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (tok0 + kq * 4 + i >= t1) acc[i] = -INFINITY;
+
+        float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const float m_cand = fmaxf(m_used, mx);  // finite: the page's first token is valid
+        const bool move = m_cand > m_used + tau_raw;
+        const bool resc = __builtin_amdgcn_ballot_w64(move) != 0;
+        if (resc) {
+            const float m_new = move ? m_cand : m_used;  // alpha = 1 for unmoved heads
+            const float alpha = fast_exp2((m_used - m_new) * scale_log2);
+            m_used = m_new;
+            l_part *= alpha;
+            if (kq == 0 && n < GH) a_lds[w][n] = alpha;
+        }
+        const float mb = m_used * scale_log2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p = fast_exp2(fmaf(acc[i], scale_log2, -mb));
+            l_part += p;
+            if (n < GH) p_lds[w][kq * 4 + i][n] = p;
+        }
+        wave_lds_fence();
+
+        if (resc) {
+#pragma unroll
+            for (int hh = 0; hh < GH; ++hh) {
+                const float a = a_lds[w][hh];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) oacc[hh][e] *= a;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const int tl = tg + TG * i;
+            const bool ok = tok0 + tl < t1;  // slots past the sequence may hold anything
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t wd = ok ? vv[i][e] : 0u;
+                x[2 * e] = bf16lo(wd);
+                x[2 * e + 1] = bf16hi(wd);
+            }
+#pragma unroll
+            for (int hh = 0; hh < GH; ++hh) {
+                const float p = p_lds[w][tl][hh];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) oacc[hh][e] = fmaf(p, x[e], oacc[hh][e]);
+            }
+        }
+        wave_lds_fence();
+    }
+
+    // ---- reduce within the wave, then across the 4 waves ----
+    float l = l_part;
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+#pragma unroll
+    for (int hh = 0; hh < GH; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = oacc[hh][e];
+#pragma unroll
+            for (int msk = CH; msk < 64; msk <<= 1) x += shfl_xor(x, msk);
+            oacc[hh][e] = x;
+        }
+    if (kq == 0 && n < GH) {
+        red_m[w][n] = m_used;
+        red_l[w][n] = l;
+    }
+    if (tg == 0) {
+#pragma unroll
+        for (int hh = 0; hh < GH; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red_o[w][hh][c * 8 + e] = oacc[hh][e];
+    }
+    __syncthreads();
+
+    for (int idx = tid; idx < nheads * D; idx += 256) {
+        const int hh = idx / D, dd = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red_m[ww][hh]);
+        float lsum = 0.f, acc = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) {
+                const float f = fast_exp2((red_m[ww][hh] - M) * scale_log2);  // 0 for empty waves
+                lsum = fmaf(f, red_l[ww][hh], lsum);
+                acc = fmaf(f, red_o[ww][hh][dd], acc);
+            }
+        }
+        const size_t row = ((size_t)s * H + h0 + hh) * max_splits + split;
+        o_part[row * D + dd] = M != -INFINITY ? acc / lsum : 0.f;
+        if (dd == 0)
+            lse_part[row] = M != -INFINITY ? M * scale_log2 + fast_log2(lsum) : -INFINITY;
+    }
+}
+
+// Merge the splits of one (sequence, head): LSE = log2 sum_k 2^lse_k (relative to the
+// largest), O = sum_k 2^(lse_k - LSE) O_k. One wave per (sequence, head).
+template <int D>
+__global__ __launch_bounds__(64) void decode_combine_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part,
+    const int32_t* __restrict__ seq_lens, uint16_t* __restrict__ o, float* __restrict__ lse,
+    int H, int max_seq_len, int split_tokens, int max_splits) {
+    constexpr int PER = D / 64;  // output dims per lane
+    const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+    const int L = min(max(seq_lens[s], 0), max_seq_len);
+    const int ns = (L + split_tokens - 1) / split_tokens;
+    const size_t row = (size_t)s * H + h;
+    const float* lp = lse_part + row * max_splits;
+
+    float M = -INFINITY;
+    for (int kk = 0; kk < ns; ++kk) M = fmaxf(M, lp[kk]);
+    float out[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) out[e] = 0.f;
+    float W = 0.f;
+    if (M != -INFINITY) {
+        for (int kk = 0; kk < ns; ++kk) {
+            const float f = fast_exp2(lp[kk] - M);
+            W += f;
+            const float* op = o_part + (row * max_splits + kk) * D + lane * PER;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) out[e] = fmaf(f, op[e], out[e]);
+        }
+        const float inv = 1.f / W;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) out[e] *= inv;
+    }
+    uint16_t* orow = o + row * D + lane * PER;
+    if constexpr (PER == 2) {
+        *reinterpret_cast<uint32_t*>(orow) = pack_bf16x2(out[0], out[1]);
+    } else {
+        orow[0] = (uint16_t)(pack_bf16x2(out[0], 0.f) & 0xffffu);
+    }
+    if (lse != nullptr && lane == 0)
+        lse[row] = M != -INFINITY ? (M + fast_log2(W)) * kLn2 : -INFINITY;
+}
+
+template <int D, int GH>
+hipError_t launch_split(const void* q, const void* kc, const void* vc, const int32_t* pt,
+                        const int32_t* sl, float* o_part, float* lse_part, int num_seqs, int H,
+                        int Hkv, int g, int n_hg, int num_pages, int max_pages, int max_seq_len,
+                        int split_tokens, int max_splits, float scale, hipStream_t stream) {
+    const float scale_log2 = scale * kLog2e;
+    const float tau_raw = 8.0f / scale_log2;
+    dim3 grid(max_splits, Hkv * n_hg, num_seqs);
+    hipLaunchKernelGGL((decode_split_kernel<D, GH>), grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+                       static_cast<const uint16_t*>(vc), pt, sl, o_part, lse_part, H, Hkv, g,
+                       n_hg, num_pages, max_pages, max_seq_len, split_tokens, max_splits,
+                       scale_log2, tau_raw);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_split_d(int GH, const void* q, const void* kc, const void* vc,
+                          const int32_t* pt, const int32_t* sl, float* o_part, float* lse_part,
+                          int num_seqs, int H, int Hkv, int g, int n_hg, int num_pages,
+                          int max_pages, int max_seq_len, int split_tokens, int max_splits,
+                          float scale, hipStream_t stream) {
+    if (GH == 4)
+        return launch_split<D, 4>(q, kc, vc, pt, sl, o_part, lse_part, num_seqs, H, Hkv, g, n_hg,
+                                  num_pages, max_pages, max_seq_len, split_tokens, max_splits,
+                                  scale, stream);
+    if (GH == 8)
+        return launch_split<D, 8>(q, kc, vc, pt, sl, o_part, lse_part, num_seqs, H, Hkv, g, n_hg,
+                                  num_pages, max_pages, max_seq_len, split_tokens, max_splits,
+                                  scale, stream);
+    return launch_split<D, 16>(q, kc, vc, pt, sl, o_part, lse_part, num_seqs, H, Hkv, g, n_hg,
+                               num_pages, max_pages, max_seq_len, split_tokens, max_splits,
+                               scale, stream);
+}
+
+}  // namespace
+
+int decode_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size) {
+    // Long splits keep the partial-result traffic small (one fp32 row of d per head
+    // and split); shorter ones are used when too few work-groups would be launched.
+    int T = 512;
+    while (T > 64 && (long long)num_seqs * Hkv * ((max_seq_len + T - 1) / T) < 2048) T >>= 1;
+    if (T < page_size) T = page_size;
+    return T;
+}
+
+size_t decode_workspace_bytes(int num_seqs, int H, int Hkv, int d, int max_seq_len,
+                              int page_size) {
+    const int T = decode_split_tokens(num_seqs, Hkv, max_seq_len, page_size);
+    const size_t max_splits = (size_t)(max_seq_len + T - 1) / T;
+    const size_t rows = (size_t)num_seqs * H * max_splits;
+    return rows * (size_t)d * sizeof(float) + rows * sizeof(float);
+}
+
+hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* page_table, const int32_t* seq_lens, void* o,
+                               float* lse, int num_seqs, int H, int Hkv, int d, int num_pages,
+                               int max_pages_per_seq, int max_seq_len, float scale,
+                               void* workspace, hipStream_t stream) {
+    const int T = decode_split_tokens(num_seqs, Hkv, max_seq_len, kPage);
+    const int max_splits = (max_seq_len + T - 1) / T;
+    const int g = H / Hkv;
+    const int GH = g <= 4 ? 4 : g <= 8 ? 8 : 16;
+    const int n_hg = g <= 16 ? 1 : g / 16;
+    float* o_part = static_cast<float*>(workspace);
+    float* lse_part = o_part + (size_t)num_seqs * H * max_splits * d;
+
+    hipError_t e = d == 128
+        ? launch_split_d<128>(GH, q, k_cache, v_cache, page_table, seq_lens, o_part, lse_part,
+                              num_seqs, H, Hkv, g, n_hg, num_pages, max_pages_per_seq,
+                              max_seq_len, T, max_splits, scale, stream)
+        : launch_split_d<64>(GH, q, k_cache, v_cache, page_table, seq_lens, o_part, lse_part,
+                             num_seqs, H, Hkv, g, n_hg, num_pages, max_pages_per_seq,
+                             max_seq_len, T, max_splits, scale, stream);
+    if (e != hipSuccess) return e;
+    dim3 grid(H, num_seqs);
+    if (d == 128)
+        hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(64), 0, stream, o_part,
+                           lse_part, seq_lens, static_cast<uint16_t*>(o), lse, H, max_seq_len, T,
+                           max_splits);
+    else
+        hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(64), 0, stream, o_part,
+                           lse_part, seq_lens, static_cast<uint16_t*>(o), lse, H, max_seq_len, T,
+                           max_splits);
+    return hipGetLastError();
+}
+
+}  // namespace kvfa

@@ -1,0 +1,31 @@
+// Host-side launchers of the attention kernels. Arguments are already validated by
+// the C ABI layer (api.hip); each launcher only enqueues work on `stream` and returns
+// the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvfa {
+
+hipError_t launch_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse,
+                           int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                           hipStream_t stream);
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                           hipStream_t stream);
+
+// Decode split plan: tokens per split-K work-group, and the workspace it implies.
+int decode_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size);
+size_t decode_workspace_bytes(int num_seqs, int H, int Hkv, int d, int max_seq_len,
+                              int page_size);
+
+hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* page_table, const int32_t* seq_lens, void* o,
+                               float* lse, int num_seqs, int H, int Hkv, int d, int num_pages,
+                               int max_pages_per_seq, int max_seq_len, float scale,
+                               void* workspace, hipStream_t stream);
+
+}  // namespace kvfa

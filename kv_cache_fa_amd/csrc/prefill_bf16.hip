@@ -1,0 +1,325 @@
+// bf16 exact attention (prefill) on gfx950 MFMA, fp32 accumulation.
+//
+// Method (page "Donanıma Duyarlı Algoritma Tasarımı: FlashAttention"):
+// * K and V are split into tiles that are staged in LDS, the CU's fast on-chip
+//   memory, while the work-group's Q rows stay in registers ("FlashAttention'ın
+//   Temelleri": tiling so the N x N score matrix never reaches HBM).
+// * Each query row keeps a running max and sum that are merged tile by tile
+//   ("Online Softmax Prensibi", steps 1-5); the output accumulator is rescaled by
+//   the same factor so one pass over K/V suffices, and it is divided by the row sum
+//   once at the end.
+// * Work is split over query rows: every work-group owns one Q tile of one (batch,
+//   head) and sweeps all of the K/V tiles it needs ("FlashAttention-2:
+//   Optimizasyonlar ve İyileştirmeler", item 1); the next K/V tile is fetched from
+//   HBM while the current one is being used (item 2).
+// * GQA: query head h reads K/V head h / (H / Hkv) (glossary entry "KV Cache
+//   (Anahtar-Değer Önbelleği)", yapayzekasozluk.tr/etiket/attention).
+//
+// gfx950 mapping (this design, not the pages'):
+// * 256 threads = 4 waves; each wave owns 32 query rows (BM = 128 rows per
+//   work-group). BN = 64 keys per tile for d = 128, 128 keys for d = 64, so a K
+//   tile is always 16 KiB; K and V^T tiles are double-buffered (64 KiB of LDS, two
+//   work-groups per CU).
+// * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//   A = K rows read from LDS, B = the wave's Q held in registers. Each lane then
+//   owns one query column, so the row max and row sum are in-lane reductions plus
+//   a single exchange with lane ^ 32.
+// * The output is also accumulated transposed, O^T += V^T P^T: B = P^T comes
+//   straight from the score registers (converted to bf16), A = V^T read from a
+//   transposed LDS copy of the V tile. The key order inside each 16-key MFMA step
+//   follows the score accumulator layout; any order is valid for a sum over keys as
+//   long as A and B agree.
+// * Softmax uses exp2 with scale*log2(e) folded into one FMA per score. The
+//   reference max used for the exponentials is only moved when the true max grows by
+//   more than 8 (log2 units); exponentials then stay below 2^8 and the result is
+//   unchanged, since softmax(x) = softmax(x - c) for any c ("FlashAttention'ın
+//   Temelleri").
+// * Causal: key tiles entirely in a row block's future are never visited; only the
+//   tiles crossing the diagonal (and a ragged last tile) pay for masking. Work is
+//   ordered longest-first, and each XCD's work-groups share the same (batch, head)
+//   group so K/V tiles are reused from that XCD's L2.
+#include "common.h"
+#include "launch.h"
+
+namespace kvfa {
+
+namespace {
+
+template <int D>
+struct Tile {
+    static constexpr int NT = 256;              // threads per work-group
+    static constexpr int BM = 128;              // query rows per work-group (32 per wave)
+    static constexpr int BN = D == 128 ? 64 : 128;  // keys per tile
+    static constexpr int CH = D / 8;            // 16-byte chunks per K/V row
+    static constexpr int KB = BN / 32;          // 32-key blocks of S^T
+    static constexpr int KS = D / 16;           // MFMA k-steps of Q.K (16 dims each)
+    static constexpr int DB = D / 32;           // 32-dim blocks of O^T
+    static constexpr int PS = BN / 16;          // MFMA k-steps of P.V (16 keys each)
+    static constexpr int K_BYTES = BN * D * 2;
+    static constexpr int V_BYTES = BN * D * 2;
+    static constexpr int STAGE = K_BYTES + V_BYTES;
+    static constexpr int KLD = BN * CH / NT;    // 16-byte K loads per thread per tile
+    static_assert(BN / 4 * CH == NT, "one 4-key x 8-dim V unit per thread");
+    static_assert(K_BYTES == 16384, "K tile is 16 KiB");
+};
+
+// Physical 16-byte chunk of K tile row `row`, logical chunk `c` (XOR swizzle so the
+// 16 rows read by a 16-lane group hit 16 different chunk positions).
+template <int D>
+__device__ __forceinline__ int k_chunk(int row, int c) {
+    if constexpr (D == 128) return c ^ (row & 15);
+    else return c ^ ((row >> 1) & 7);
+}
+
+// Physical 8-byte group of V^T row `d` for logical key group `kg` (keys 4kg..4kg+3).
+// Conflict-free for the MFMA reads (32 consecutive d at one key group) and at most
+// two-way for the transposing writes.
+template <int BN>
+__device__ __forceinline__ int vt_group(int d, int kg) {
+    if constexpr (BN == 64) return kg ^ (((d >> 1) ^ (d >> 3)) & 15);
+    else return kg ^ (((d >> 1) ^ ((d & 1) << 4)) & 31);
+}
+
+// Work-group id -> (batch*H + head, q tile). Causal tiles run longest first. When
+// the (batch, head) count is a multiple of 8, the i-th work-group (which the
+// dispatcher places on XCD i % 8) is given a (batch, head) from a contiguous block
+// owned by that XCD, so neighbouring heads (which share K/V under GQA) and the same
+// K/V ranges meet in one L2.
+__device__ __forceinline__ void map_work(int id, int n_qt, int BH, bool causal, int& pair,
+                                         int& qt) {
+    int r;
+    if ((BH & 7) == 0) {
+        const int per = BH >> 3, slot = id >> 3;
+        pair = (id & 7) * per + slot % per;
+        r = slot / per;
+    } else {
+        pair = id % BH;
+        r = id / BH;
+    }
+    qt = causal ? n_qt - 1 - r : r;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
+                     float* __restrict__ lse, int H, int Hkv, int Nq, int Nk, int n_qt,
+                     int BH, float scale_log2, float tau_raw) {
+    using T = Tile<D>;
+    constexpr int BN = T::BN;
+    __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int col = lane & 31;      // query column of S^T / O^T owned by this lane
+    const int g = lane >> 5;        // which half of the k-slots this lane supplies
+
+    int pair, qt;
+    map_work(blockIdx.x, n_qt, BH, CAUSAL, pair, qt);
+    const int b = pair / H, h = pair % H;
+    const int kvh = h / (H / Hkv);
+    const int q0 = qt * T::BM;
+    const int off = Nk - Nq;
+    const int qrow = q0 + w * 32 + col;
+
+    const auto rq = make_rsrc(q + (size_t)pair * Nq * D, (uint32_t)Nq * D * 2);
+    const auto rk = make_rsrc(k + ((size_t)b * Hkv + kvh) * Nk * D, (uint32_t)Nk * D * 2);
+    const auto rv = make_rsrc(v + ((size_t)b * Hkv + kvh) * Nk * D, (uint32_t)Nk * D * 2);
+
+    // B operand of S^T = K Q^T: Q[qrow][16s + 8g .. +7]; rows past Nq load as zero.
+    u32x4 qf[T::KS];
+#pragma unroll
+    for (int s = 0; s < T::KS; ++s)
+        qf[s] = buf_load16(rq, (uint32_t)(qrow * D + s * 16 + g * 8) * 2);
+
+    // Tiles to visit and the first one that needs a mask.
+    const int n_all = (Nk + BN - 1) / BN;
+    int n_tiles = n_all, full = Nk / BN;
+    if (CAUSAL) {
+        const int last_row = min(q0 + T::BM, Nq) - 1;
+        n_tiles = min(n_all, (last_row + off) / BN + 1);
+        full = min(full, (q0 + off + 1) / BN);
+    }
+
+    // Global -> register staging of one K/V tile.
+    u32x4 kr[T::KLD], vr[4];
+    const int vkg = tid / T::CH, vc = tid % T::CH;  // this thread's V unit
+    auto load_tile = [&](int j) {
+        const int kb0 = j * BN;
+#pragma unroll
+        for (int i = 0; i < T::KLD; ++i) {
+            const int e = tid + T::NT * i, row = e / T::CH, c = e % T::CH;
+            kr[i] = buf_load16(rk, (uint32_t)((kb0 + row) * D + c * 8) * 2);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            vr[r] = buf_load16(rv, (uint32_t)((kb0 + vkg * 4 + r) * D + vc * 8) * 2);
+    };
+    // Register -> LDS: K swizzled row-major, V transposed to V^T[d][key].
+    auto store_tile = [&](int stage) {
+        char* ks = smem + stage * T::STAGE;
+        char* vs = ks + T::K_BYTES;
+#pragma unroll
+        for (int i = 0; i < T::KLD; ++i) {
+            const int e = tid + T::NT * i, row = e / T::CH, c = e % T::CH;
+            *reinterpret_cast<u32x4*>(ks + row * D * 2 + k_chunk<D>(row, c) * 16) = kr[i];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t lo = __builtin_amdgcn_perm(vr[1][e >> 1], vr[0][e >> 1], sel);
+            const uint32_t hi = __builtin_amdgcn_perm(vr[3][e >> 1], vr[2][e >> 1], sel);
+            const int d = vc * 8 + e;
+            u32x2 pk = {lo, hi};
+            *reinterpret_cast<u32x2*>(vs + d * BN * 2 + vt_group<BN>(d, vkg) * 8) = pk;
+        }
+    };
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    float m_used = -INFINITY;  // raw-score reference max of this lane's query
+    float l_part = 0.f;        // this lane's share of the row sum
+    f32x16 oacc[T::DB];
+#pragma unroll
+    for (int i = 0; i < T::DB; ++i) oacc[i] = f32x16{};
+
+    for (int j = 0; j < n_tiles; ++j) {
+        const int cur = j & 1;
+        if (j + 1 < n_tiles) load_tile(j + 1);
+        const char* ks = smem + cur * T::STAGE;
+        const char* vs = ks + T::K_BYTES;
+
+        // ---- S^T = K Q^T for this tile ----
+        f32x16 sacc[T::KB];
+#pragma unroll
+        for (int kb = 0; kb < T::KB; ++kb) {
+            sacc[kb] = f32x16{};
+            const int row = kb * 32 + col;
+#pragma unroll
+            for (int s = 0; s < T::KS; ++s) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(
+                    ks + row * D * 2 + k_chunk<D>(row, 2 * s + g) * 16);
+                sacc[kb] = mfma32x32x16(a, qf[s], sacc[kb]);
+            }
+        }
+
+        // ---- mask (diagonal / ragged tiles only) ----
+        if (j >= full) {
+#pragma unroll
+            for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = j * BN + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+                    const bool dead = key >= Nk || (CAUSAL && key > qrow + off);
+                    if (dead) sacc[kb][i] = -INFINITY;
+                }
+        }
+
+        // ---- online softmax ----
+        // Every row attends key 0 (causal rows see the whole prefix), so after the
+        // first tile the max is finite and no -inf - -inf can occur.
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+        mx = fmaxf(mx, xor32(mx));
+        const float m_cand = fmaxf(m_used, mx);
+        const bool move = m_cand > m_used + tau_raw;
+        if (__builtin_amdgcn_ballot_w64(move)) {
+            // Only rows whose max moved change their reference (alpha = 1 elsewhere), so
+            // a row's arithmetic never depends on the other rows of the wave.
+            const float m_new = move ? m_cand : m_used;
+            const float alpha = fast_exp2((m_used - m_new) * scale_log2);
+            m_used = m_new;
+            l_part *= alpha;
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        }
+        const float mb = m_used * scale_log2;
+#pragma unroll
+        for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -mb));
+                l_part += p;
+                sacc[kb][i] = p;
+            }
+
+        // ---- O^T += V^T P^T ----
+#pragma unroll
+        for (int t = 0; t < T::PS; ++t) {
+            const int kb = t >> 1, base = (t & 1) * 8;
+            u32x4 pf;
+            pf[0] = pack_bf16x2(sacc[kb][base + 0], sacc[kb][base + 1]);
+            pf[1] = pack_bf16x2(sacc[kb][base + 2], sacc[kb][base + 3]);
+            pf[2] = pack_bf16x2(sacc[kb][base + 4], sacc[kb][base + 5]);
+            pf[3] = pack_bf16x2(sacc[kb][base + 6], sacc[kb][base + 7]);
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db) {
+                const int d = db * 32 + col;
+                const char* vrow = vs + d * BN * 2;
+                const u32x2 a0 = *reinterpret_cast<const u32x2*>(
+                    vrow + vt_group<BN>(d, 4 * t + g) * 8);
+                const u32x2 a1 = *reinterpret_cast<const u32x2*>(
+                    vrow + vt_group<BN>(d, 4 * t + 2 + g) * 8);
+                const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
+                oacc[db] = mfma32x32x16(a, pf, oacc[db]);
+            }
+        }
+
+        if (j + 1 < n_tiles) store_tile(cur ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = O_acc / l, lse = M + ln L ----
+    const float l = l_part + xor32(l_part);
+    if (qrow < Nq) {
+        const float inv = 1.f / l;
+        uint16_t* orow = o + ((size_t)pair * Nq + qrow) * D;
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d0 = db * 32 + r * 8 + g * 4;
+                u32x2 pk = {pack_bf16x2(oacc[db][r * 4 + 0] * inv, oacc[db][r * 4 + 1] * inv),
+                            pack_bf16x2(oacc[db][r * 4 + 2] * inv, oacc[db][r * 4 + 3] * inv)};
+                *reinterpret_cast<u32x2*>(orow + d0) = pk;
+            }
+        if (lse != nullptr && g == 0)
+            lse[(size_t)pair * Nq + qrow] = (m_used * scale_log2 + fast_log2(l)) * kLn2;
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_typed(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int H, int Hkv, int Nq, int Nk, float scale, hipStream_t stream) {
+    using T = Tile<D>;
+    const int n_qt = (Nq + T::BM - 1) / T::BM;
+    const int BH = B * H;
+    const float scale_log2 = scale * kLog2e;
+    const float tau_raw = 8.0f / scale_log2;  // move the reference max past +8 in log2 units
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(n_qt * BH), dim3(T::NT), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, H, Hkv,
+                       Nq, Nk, n_qt, BH, scale_log2, tau_raw);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                           hipStream_t stream) {
+    if (d == 128)
+        return causal ? launch_typed<128, true>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream)
+                      : launch_typed<128, false>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream);
+    return causal ? launch_typed<64, true>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream)
+                  : launch_typed<64, false>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream);
+}
+
+}  // namespace kvfa

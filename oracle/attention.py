@@ -95,7 +95,6 @@ def attention(q, k, v, *, causal: bool, scale: float, rows=None, return_probs=Fa
     if H % Hkv:
         raise ValueError("H must be a multiple of Hkv")
     g = H // Hkv
-    full_mask = allowed_keys(Nq, Nk, causal)
 
     pairs = [(b, h) for b in range(B) for h in range(H)] if rows is None else sorted(rows)
     outs, lses, probs = {}, {}, {}
@@ -104,7 +103,9 @@ def attention(q, k, v, *, causal: bool, scale: float, rows=None, return_probs=Fa
         kvh = h // g
         # full score rows: (len(idx) x Nk), the "compatibility matrix" restricted to idx
         S = scale * (q[b, h, idx, :] @ k[b, kvh].T)
-        P, m, l = softmax_rows(S, full_mask[idx])
+        mask = np.ones(S.shape, dtype=bool) if not causal else \
+            (np.arange(Nk)[None, :] <= idx[:, None] + (Nk - Nq))
+        P, m, l = softmax_rows(S, mask)
         O = P @ v[b, kvh]
         with np.errstate(divide="ignore"):
             lse = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), NEG_INF)

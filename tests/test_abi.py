@@ -1,0 +1,116 @@
+"""The C-ABI library loads, exports every declared symbol and rejects bad arguments.
+
+CPU only: every call below fails validation on the host and returns before any HIP
+call (the pointers are fake, aligned, non-null integers that are never
+dereferenced). No call here ever reaches a kernel launch.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from kv_cache_fa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvfa.h")
+
+INVALID, UNSUPPORTED = _lib.FA_ERR_INVALID, _lib.FA_ERR_UNSUPPORTED
+P = 1 << 20          # a fake, 16-byte aligned device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^(?:int|size_t|const char\*)\s+(\w+)\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libkvfa.so not built (run __graft_entry__.build())")
+    return _lib.lib()
+
+
+def test_header_declares_the_expected_entry_points():
+    assert set(declared_functions()) == {
+        "fa_fwd", "fa_fwd_fp32", "fa_decode_paged", "fa_decode_paged_workspace_size",
+        "fa_decode_paged_split_tokens", "fa_status_string"}
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, name
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, 7):
+        assert _lib.fa_status_string(st)
+    assert _lib.fa_status_string(-1).startswith("FA_ERR_INVALID")
+
+
+def _fwd(lib, fn="fa_fwd", q=P, k=P, v=P, o=P, lse=None, B=1, H=8, Hkv=8, Nq=64, Nk=64, d=128,
+         causal=1, scale=0.125):
+    return getattr(lib, fn)(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_fp32"])
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(k=P + 8), INVALID),
+    (dict(lse=P + 2), INVALID),
+    (dict(B=0), INVALID), (dict(H=0), INVALID), (dict(Nq=0), INVALID), (dict(Nk=-3), INVALID),
+    (dict(H=8, Hkv=3), INVALID), (dict(Hkv=0), INVALID),
+    (dict(causal=1, Nq=65, Nk=64), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID), (dict(scale=math.inf), INVALID),
+    (dict(scale=math.nan), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(d=32), UNSUPPORTED),
+    (dict(Nk=1 << 23, causal=0), UNSUPPORTED),
+])
+def test_prefill_validation(lib, fn, kw, want):
+    assert _fwd(lib, fn, **kw) == want
+
+
+def _dec(lib, q=P, kc=P, vc=P, pt=P, sl=P, page_size=16, o=P, lse=None, S=4, H=32, Hkv=8,
+         d=128, num_pages=100, max_pages=8, max_seq_len=128, scale=0.09, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_decode_paged_workspace_size(S, H, Hkv, d, max_seq_len, page_size) \
+            if page_size == 16 and d in (64, 128) else 1 << 30
+    return lib.fa_decode_paged(q, kc, vc, pt, sl, page_size, o, lse, S, H, Hkv, d, num_pages,
+                               max_pages, max_seq_len, scale, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(pt=None), INVALID), (dict(sl=None), INVALID),
+    (dict(ws=None), INVALID), (dict(kc=P + 4), INVALID), (dict(pt=P + 2), INVALID),
+    (dict(S=0), INVALID), (dict(num_pages=0), INVALID), (dict(max_pages=0), INVALID),
+    (dict(max_seq_len=0), INVALID), (dict(H=32, Hkv=5), INVALID),
+    (dict(max_pages=7, max_seq_len=128), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=math.nan), INVALID),
+    (dict(ws_bytes=16), INVALID),
+    (dict(page_size=32, max_pages=4), UNSUPPORTED), (dict(d=80), UNSUPPORTED),
+    (dict(H=40, Hkv=2), UNSUPPORTED),   # group of 20 query heads
+])
+def test_decode_validation(lib, kw, want):
+    assert _dec(lib, **kw) == want
+
+
+def test_workspace_size(lib):
+    f = lib.fa_decode_paged_workspace_size
+    assert f(64, 32, 8, 128, 8192, 16) > 0
+    assert f(0, 32, 8, 128, 8192, 16) == 0
+    assert f(64, 32, 8, 100, 8192, 16) == 0
+    assert f(64, 32, 8, 128, 8192, 8) == 0
+    T = lib.fa_decode_paged_split_tokens(64, 8, 8192, 16)
+    assert T % 16 == 0 and T >= 16
+    splits = -(-8192 // T)
+    assert f(64, 32, 8, 128, 8192, 16) == 64 * 32 * splits * (128 + 1) * 4
+    # few sequences: shorter splits keep enough work-groups in flight
+    assert lib.fa_decode_paged_split_tokens(1, 1, 8192, 16) < T
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        _lib.fa_fwd(x, x, x, x, causal=False, scale=0.125)
