@@ -38,6 +38,8 @@
 //   tiles crossing the diagonal (and a ragged last tile) pay for masking. Work is
 //   ordered longest-first, and each XCD's work-groups share the same (batch, head)
 //   group so K/V tiles are reused from that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -49,36 +51,24 @@ template <int D>
 struct Tile {
     static constexpr int NT = 256;              // threads per work-group
     static constexpr int BM = 128;              // query rows per work-group (32 per wave)
-    static constexpr int BN = D == 128 ? 64 : 128;  // keys per tile
+    static constexpr int BN = 64;               // keys per tile
     static constexpr int CH = D / 8;            // 16-byte chunks per K/V row
     static constexpr int KB = BN / 32;          // 32-key blocks of S^T
     static constexpr int KS = D / 16;           // MFMA k-steps of Q.K (16 dims each)
     static constexpr int DB = D / 32;           // 32-dim blocks of O^T
     static constexpr int PS = BN / 16;          // MFMA k-steps of P.V (16 keys each)
-    static constexpr int K_BYTES = BN * D * 2;
-    static constexpr int V_BYTES = BN * D * 2;
+    // Row pitches (bytes). K rows are padded by one 16-byte unit so the 16 rows read by a
+    // 16-lane group fall in 16 different bank groups; V rows are padded so the four rows
+    // gathered by one transposing read land 64 bytes apart in the bank space.
+    static constexpr int K_PITCH = D * 2 + 16;
+    static constexpr int V_PITCH = D * 2 + 64;
+    static constexpr int K_BYTES = BN * K_PITCH;
+    static constexpr int V_BYTES = BN * V_PITCH;
     static constexpr int STAGE = K_BYTES + V_BYTES;
-    static constexpr int KLD = BN * CH / NT;    // 16-byte K loads per thread per tile
-    static_assert(BN / 4 * CH == NT, "one 4-key x 8-dim V unit per thread");
-    static_assert(K_BYTES == 16384, "K tile is 16 KiB");
+    static constexpr int LD = BN * CH / NT;     // 16-byte chunks per thread per tile, each of K, V
+    static_assert((K_PITCH / 16) % 2 == 1, "odd K pitch in 16-byte units");
+    static_assert((V_PITCH / 16) % 16 == 4 || (V_PITCH / 16) % 16 == 12, "V pitch = 4 (mod 16) units");
 };
-
-// Physical 16-byte chunk of K tile row `row`, logical chunk `c` (XOR swizzle so the
-// 16 rows read by a 16-lane group hit 16 different chunk positions).
-template <int D>
-__device__ __forceinline__ int k_chunk(int row, int c) {
-    if constexpr (D == 128) return c ^ (row & 15);
-    else return c ^ ((row >> 1) & 7);
-}
-
-// Physical 8-byte group of V^T row `d` for logical key group `kg` (keys 4kg..4kg+3).
-// Conflict-free for the MFMA reads (32 consecutive d at one key group) and at most
-// two-way for the transposing writes.
-template <int BN>
-__device__ __forceinline__ int vt_group(int d, int kg) {
-    if constexpr (BN == 64) return kg ^ (((d >> 1) ^ (d >> 3)) & 15);
-    else return kg ^ (((d >> 1) ^ ((d & 1) << 4)) & 31);
-}
 
 // Work-group id -> (batch*H + head, q tile). Causal tiles run longest first. When
 // the (batch, head) count is a multiple of 8, the i-th work-group (which the
@@ -97,6 +87,17 @@ __device__ __forceinline__ void map_work(int id, int n_qt, int BH, bool causal, 
         r = id / BH;
     }
     qt = causal ? n_qt - 1 - r : r;
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each 16-lane group, source lane
+// a + 4e points at 4 consecutive bf16 of row e (e = 0..3), column block a; lane i of
+// the group receives column i of rows 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) char*)p);
+    return __builtin_bit_cast(u32x2, v);
 }
 
 template <int D, bool CAUSAL>
@@ -141,37 +142,32 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         full = min(full, (q0 + off + 1) / BN);
     }
 
-    // Global -> register staging of one K/V tile.
-    u32x4 kr[T::KLD], vr[4];
-    const int vkg = tid / T::CH, vc = tid % T::CH;  // this thread's V unit
+    // Per-lane LDS byte offsets (stage-relative); every other term is an immediate.
+    const int k_lane = col * T::K_PITCH + g * 16;
+    const int vG = lane >> 4, vj = lane & 15;
+    const int v_lane = T::K_BYTES + ((vG >> 1) * 4 + (vj >> 2)) * T::V_PITCH + 32 * (vG & 1) +
+                       8 * (vj & 3);
+
+    // Global -> register staging of one K/V tile (rows past Nk load as zero).
+    u32x4 kr[T::LD], vr[T::LD];
     auto load_tile = [&](int j) {
         const int kb0 = j * BN;
 #pragma unroll
-        for (int i = 0; i < T::KLD; ++i) {
+        for (int i = 0; i < T::LD; ++i) {
             const int e = tid + T::NT * i, row = e / T::CH, c = e % T::CH;
-            kr[i] = buf_load16(rk, (uint32_t)((kb0 + row) * D + c * 8) * 2);
+            const uint32_t go = (uint32_t)((kb0 + row) * D + c * 8) * 2;
+            kr[i] = buf_load16(rk, go);
+            vr[i] = buf_load16(rv, go);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            vr[r] = buf_load16(rv, (uint32_t)((kb0 + vkg * 4 + r) * D + vc * 8) * 2);
     };
-    // Register -> LDS: K swizzled row-major, V transposed to V^T[d][key].
     auto store_tile = [&](int stage) {
         char* ks = smem + stage * T::STAGE;
         char* vs = ks + T::K_BYTES;
 #pragma unroll
-        for (int i = 0; i < T::KLD; ++i) {
+        for (int i = 0; i < T::LD; ++i) {
             const int e = tid + T::NT * i, row = e / T::CH, c = e % T::CH;
-            *reinterpret_cast<u32x4*>(ks + row * D * 2 + k_chunk<D>(row, c) * 16) = kr[i];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            const uint32_t lo = __builtin_amdgcn_perm(vr[1][e >> 1], vr[0][e >> 1], sel);
-            const uint32_t hi = __builtin_amdgcn_perm(vr[3][e >> 1], vr[2][e >> 1], sel);
-            const int d = vc * 8 + e;
-            u32x2 pk = {lo, hi};
-            *reinterpret_cast<u32x2*>(vs + d * BN * 2 + vt_group<BN>(d, vkg) * 8) = pk;
+            *reinterpret_cast<u32x4*>(ks + row * T::K_PITCH + c * 16) = kr[i];
+            *reinterpret_cast<u32x4*>(vs + row * T::V_PITCH + c * 16) = vr[i];
         }
     };
 
@@ -185,38 +181,38 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < T::DB; ++i) oacc[i] = f32x16{};
 
-    for (int j = 0; j < n_tiles; ++j) {
+    // One K/V tile: scores, (mask), online softmax, P.V, then stage the prefetched tile.
+    auto tile = [&](const int j, auto masked) {
         const int cur = j & 1;
         if (j + 1 < n_tiles) load_tile(j + 1);
-        const char* ks = smem + cur * T::STAGE;
-        const char* vs = ks + T::K_BYTES;
+        const char* kl = smem + cur * T::STAGE + k_lane;
+        const char* vl = smem + cur * T::STAGE + v_lane;
 
         // ---- S^T = K Q^T for this tile ----
         f32x16 sacc[T::KB];
 #pragma unroll
         for (int kb = 0; kb < T::KB; ++kb) {
             sacc[kb] = f32x16{};
-            const int row = kb * 32 + col;
 #pragma unroll
             for (int s = 0; s < T::KS; ++s) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(
-                    ks + row * D * 2 + k_chunk<D>(row, 2 * s + g) * 16);
+                const u32x4 a =
+                    *reinterpret_cast<const u32x4*>(kl + kb * 32 * T::K_PITCH + s * 32);
                 sacc[kb] = mfma32x32x16(a, qf[s], sacc[kb]);
             }
         }
 
         // ---- mask (diagonal / ragged tiles only) ----
-        if (j >= full) {
+        if constexpr (decltype(masked)::value) {
+            // key offset inside the tile of element (kb, i) is kb*32 + 8*(i/4) + 4g + i%4;
+            // it is dead past the row's last key and past Nk.
+            int lim = Nk - 1 - j * BN - 4 * g;
+            if (CAUSAL) lim = min(lim, qrow + off - j * BN - 4 * g);
 #pragma unroll
             for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = j * BN + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-                    const bool dead = key >= Nk || (CAUSAL && key > qrow + off);
-                    if (dead) sacc[kb][i] = -INFINITY;
-                }
+                for (int i = 0; i < 16; ++i)
+                    if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sacc[kb][i] = -INFINITY;
         }
-
         // ---- online softmax ----
         // Every row attends key 0 (causal rows see the whole prefix), so after the
         // first tile the max is finite and no -inf - -inf can occur.
@@ -261,12 +257,9 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             pf[3] = pack_bf16x2(sacc[kb][base + 6], sacc[kb][base + 7]);
 #pragma unroll
             for (int db = 0; db < T::DB; ++db) {
-                const int d = db * 32 + col;
-                const char* vrow = vs + d * BN * 2;
-                const u32x2 a0 = *reinterpret_cast<const u32x2*>(
-                    vrow + vt_group<BN>(d, 4 * t + g) * 8);
-                const u32x2 a1 = *reinterpret_cast<const u32x2*>(
-                    vrow + vt_group<BN>(d, 4 * t + 2 + g) * 8);
+                // keys 16t + 4g + {0..3} and 16t + 8 + 4g + {0..3} at dim 32db + col
+                const u32x2 a0 = lds_read_tr(vl + (t * 16) * T::V_PITCH + 64 * db);
+                const u32x2 a1 = lds_read_tr(vl + (t * 16 + 8) * T::V_PITCH + 64 * db);
                 const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
                 oacc[db] = mfma32x32x16(a, pf, oacc[db]);
             }
@@ -274,7 +267,11 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
         if (j + 1 < n_tiles) store_tile(cur ^ 1);
         __syncthreads();
-    }
+    };
+
+    const int n_plain = min(full, n_tiles);
+    for (int j = 0; j < n_plain; ++j) tile(j, std::false_type{});
+    for (int j = n_plain; j < n_tiles; ++j) tile(j, std::true_type{});
 
     // ---- epilogue: O = O_acc / l, lse = M + ln L ----
     const float l = l_part + xor32(l_part);
