@@ -50,8 +50,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     __shared__ float red_o[kWaves][GH][D];
 
     const int s = blockIdx.z;
-    const int kvh = blockIdx.y / n_hg, hg = blockIdx.y % n_hg;
-    const int split = blockIdx.x;
+    const int kvh = blockIdx.x / n_hg, hg = blockIdx.x % n_hg;
+    const int split = blockIdx.y;
     const int L = min(max(seq_lens[s], 0), max_seq_len);
     const int t0 = split * split_tokens;
     if (t0 >= L) return;  // uniform: this split holds no cached token
@@ -59,7 +59,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const int first_page = t0 / kPage;
     const int n_pg = (t1 - t0 + kPage - 1) / kPage;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
     const int n = lane & 15;     // head column of S^T held by this lane
     const int kq = lane >> 4;    // k-slot group / token quad of S^T
     const int tg = lane / CH, c = lane % CH;  // P.V layout: token group, V chunk
@@ -84,80 +85,106 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) oacc[hh][e] = 0.f;
 
-    for (int pi = w; pi < n_pg; pi += kWaves) {
-        const int pidx = first_page + pi;
-        const int pid = __builtin_amdgcn_readfirstlane(page_table[(size_t)s * max_pages + pidx]);
-        if ((unsigned)pid >= (unsigned)num_pages) continue;  // never dereference a bad id
-        const size_t page_base = (size_t)pid * kPage * tok_stride + (size_t)kvh * D;
-        const int tok0 = pidx * kPage;
+    // This wave's pages are first_page + w + kWaves*i, i < n_my. Lane i holds the
+    // physical id of the i-th one, so no page-table load sits on the loop's critical path.
+    const int n_my = w < n_pg ? (n_pg - w + kWaves - 1) / kWaves : 0;
+    int pid_lane = -1;
+    if (lane < n_my) pid_lane = page_table[(size_t)s * max_pages + first_page + w + kWaves * lane];
+    // Let the ids arrive once, here; afterwards the register no longer counts as a pending
+    // load, so reading it inside the loop does not wait for the page loads in flight.
+    __asm__ volatile("" : "+v"(pid_lane));
 
-        u32x4 kf[KS], vv[TPL];
+    // Issue the loads of the wave's it-th page (K rows as the MFMA A operand, V chunks for
+    // the P.V lanes). Returns false for an out-of-range page id, which is never read.
+    // Loads are issued unconditionally (a zero-size descriptor for an invalid page id
+    // makes them return zeros without touching memory), so the wait counts stay exact.
+    const uint32_t span = (uint32_t)((kPage - 1) * tok_stride + D) * 2;
+    const uint32_t k_off = (uint32_t)(n * tok_stride) * 2 + kq * 16;
+    const uint32_t v_off = (uint32_t)(tg * tok_stride + c * 8) * 2;
+    auto load_page = [&](int it, u32x4 (&kf)[KS], u32x4 (&vv)[TPL]) -> bool {
+        const int pid = __builtin_amdgcn_readlane(pid_lane, it);
+        const bool valid = (unsigned)pid < (unsigned)num_pages;
+        const size_t page_base = (size_t)(valid ? pid : 0) * kPage * tok_stride + (size_t)kvh * D;
+        const auto rk = make_rsrc(kcache + page_base, valid ? span : 0u);
+        const auto rv = make_rsrc(vcache + page_base, valid ? span : 0u);
 #pragma unroll
-        for (int j = 0; j < KS; ++j)
-            kf[j] = *reinterpret_cast<const u32x4*>(kcache + page_base + n * tok_stride +
-                                                     (j * 4 + kq) * 8);
+        for (int j = 0; j < KS; ++j) kf[j] = buf_load16(rk, k_off + j * 64);
 #pragma unroll
-        for (int i = 0; i < TPL; ++i)
-            vv[i] = *reinterpret_cast<const u32x4*>(vcache + page_base +
-                                                     (tg + TG * i) * tok_stride + c * 8);
+        for (int i = 0; i < TPL; ++i) vv[i] = buf_load16(rv, v_off + (uint32_t)(TG * i * tok_stride) * 2);
+        return valid;
+    };
 
-        // S^T: acc[i] = score of token 4*kq + i for head column n
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < KS; ++j) acc = mfma16x16x32(kf[j], qf[j], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (tok0 + kq * 4 + i >= t1) acc[i] = -INFINITY;
+    u32x4 kA[KS], vA[TPL], kB[KS], vB[TPL];
+    bool okA = load_page(0, kA, vA);   // a lane past the wave's pages holds id -1
+    bool okB = false;
+    auto page_compute = [&](const u32x4 (&KF)[KS], const u32x4 (&VV)[TPL], const bool OK, const int IT) {
+        if (OK) {
+            const int tok0 = (first_page + w + kWaves * IT) * kPage;
 
-        float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float m_cand = fmaxf(m_used, mx);  // finite: the page's first token is valid
-        const bool move = m_cand > m_used + tau_raw;
-        const bool resc = __builtin_amdgcn_ballot_w64(move) != 0;
-        if (resc) {
-            const float m_new = move ? m_cand : m_used;  // alpha = 1 for unmoved heads
-            const float alpha = fast_exp2((m_used - m_new) * scale_log2);
-            m_used = m_new;
-            l_part *= alpha;
-            if (kq == 0 && n < GH) a_lds[w][n] = alpha;
-        }
-        const float mb = m_used * scale_log2;
+            // S^T: acc[i] = score of token 4*kq + i for head column n
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float p = fast_exp2(fmaf(acc[i], scale_log2, -mb));
-            l_part += p;
-            if (n < GH) p_lds[w][kq * 4 + i][n] = p;
-        }
-        wave_lds_fence();
+            for (int j = 0; j < KS; ++j) acc = mfma16x16x32(KF[j], qf[j], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (tok0 + kq * 4 + i >= t1) acc[i] = -INFINITY;
 
-        if (resc) {
-#pragma unroll
-            for (int hh = 0; hh < GH; ++hh) {
-                const float a = a_lds[w][hh];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) oacc[hh][e] *= a;
+            float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+            mx = fmaxf(mx, shfl_xor(mx, 16));
+            mx = fmaxf(mx, shfl_xor(mx, 32));
+            const float m_cand = fmaxf(m_used, mx);  // finite: a page's first token is valid
+            const bool move = m_cand > m_used + tau_raw;
+            const bool resc = __builtin_amdgcn_ballot_w64(move) != 0;
+            if (resc) {
+                const float m_new = move ? m_cand : m_used;  // alpha = 1 for unmoved heads
+                const float alpha = fast_exp2((m_used - m_new) * scale_log2);
+                m_used = m_new;
+                l_part *= alpha;
+                if (kq == 0 && n < GH) a_lds[w][n] = alpha;
             }
-        }
+            const float mb = m_used * scale_log2;
 #pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const int tl = tg + TG * i;
-            const bool ok = tok0 + tl < t1;  // slots past the sequence may hold anything
-            float x[8];
+            for (int i = 0; i < 4; ++i) {
+                const float p = fast_exp2(fmaf(acc[i], scale_log2, -mb));
+                l_part += p;
+                if (n < GH) p_lds[w][kq * 4 + i][n] = p;
+            }
+            wave_lds_fence();
+
+            if (resc) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t wd = ok ? vv[i][e] : 0u;
-                x[2 * e] = bf16lo(wd);
-                x[2 * e + 1] = bf16hi(wd);
+                for (int hh = 0; hh < GH; ++hh) {
+                    const float a = a_lds[w][hh];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) oacc[hh][e] *= a;
+                }
             }
 #pragma unroll
-            for (int hh = 0; hh < GH; ++hh) {
-                const float p = p_lds[w][tl][hh];
+            for (int i = 0; i < TPL; ++i) {
+                const int tl = tg + TG * i;
+                const bool ok = tok0 + tl < t1;  // slots past the sequence may hold anything
+                float x[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) oacc[hh][e] = fmaf(p, x[e], oacc[hh][e]);
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t wd = ok ? VV[i][e] : 0u;
+                    x[2 * e] = bf16lo(wd);
+                    x[2 * e + 1] = bf16hi(wd);
+                }
+#pragma unroll
+                for (int hh = 0; hh < GH; ++hh) {
+                    const float p = p_lds[w][tl][hh];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) oacc[hh][e] = fmaf(p, x[e], oacc[hh][e]);
+                }
             }
+            wave_lds_fence();
         }
-        wave_lds_fence();
+    };
+    for (int it = 0; it < n_my; it += 2) {
+        okB = load_page(it + 1, kB, vB);
+        page_compute(kA, vA, okA, it);
+        okA = load_page(it + 2, kA, vA);
+        page_compute(kB, vB, okB, it + 1);
     }
 
     // ---- reduce within the wave, then across the 4 waves ----
@@ -255,7 +282,10 @@ hipError_t launch_split(const void* q, const void* kc, const void* vc, const int
                         int split_tokens, int max_splits, float scale, hipStream_t stream) {
     const float scale_log2 = scale * kLog2e;
     const float tau_raw = 8.0f / scale_log2;
-    dim3 grid(max_splits, Hkv * n_hg, num_seqs);
+    // KV heads vary fastest: the work-groups covering one token range of one sequence
+    // are dispatched together, so each physical page (all KV heads of 16 slots, contiguous)
+    // is read by concurrently running work-groups.
+    dim3 grid(Hkv * n_hg, max_splits, num_seqs);
     hipLaunchKernelGGL((decode_split_kernel<D, GH>), grid, dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                        static_cast<const uint16_t*>(vc), pt, sl, o_part, lse_part, H, Hkv, g,
@@ -288,6 +318,8 @@ hipError_t launch_split_d(int GH, const void* q, const void* kc, const void* vc,
 int decode_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size) {
     // Long splits keep the partial-result traffic small (one fp32 row of d per head
     // and split); shorter ones are used when too few work-groups would be launched.
+    // (T <= 512 keeps every wave's page count, plus the two pages it prefetches past its
+    // last one, within the 64 lanes that hold its page ids.)
     int T = 512;
     while (T > 64 && (long long)num_seqs * Hkv * ((max_seq_len + T - 1) / T) < 2048) T >>= 1;
     if (T < page_size) T = page_size;
