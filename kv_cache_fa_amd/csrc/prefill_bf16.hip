@@ -70,18 +70,26 @@ struct Tile {
     static_assert((V_PITCH / 16) % 16 == 4 || (V_PITCH / 16) % 16 == 12, "V pitch = 4 (mod 16) units");
 };
 
-// Work-group id -> (batch*H + head, q tile). Causal tiles run longest first. When
-// the (batch, head) count is a multiple of 8, the i-th work-group (which the
-// dispatcher places on XCD i % 8) is given a (batch, head) from a contiguous block
-// owned by that XCD, so neighbouring heads (which share K/V under GQA) and the same
-// K/V ranges meet in one L2.
-__device__ __forceinline__ void map_work(int id, int n_qt, int BH, bool causal, int& pair,
-                                         int& qt) {
+// Work-group id -> (batch*H + head, q tile). The dispatcher places work-group i on XCD
+// i % 8, and each XCD has its own L2. When the (batch, head) count is a multiple of 8,
+// XCD x owns a contiguous block of (batch, head) pairs; if that block holds whole GQA
+// groups (the g query heads that read one K/V head), the XCD finishes one group's q
+// tiles before starting the next, so its L2 only has to hold one K/V head at a time.
+// Within that order causal q tiles run longest first.
+__device__ __forceinline__ void map_work(int id, int n_qt, int BH, int g, bool causal,
+                                         int& pair, int& qt) {
     int r;
     if ((BH & 7) == 0) {
-        const int per = BH >> 3, slot = id >> 3;
-        pair = (id & 7) * per + slot % per;
-        r = slot / per;
+        const int per = BH >> 3, slot = id >> 3, x = id & 7;
+        if (per % g == 0) {
+            const int span = g * n_qt;              // work-groups of one GQA group
+            const int grp = slot / span, rem = slot % span;
+            pair = x * per + grp * g + rem % g;
+            r = rem / g;
+        } else {
+            pair = x * per + slot % per;
+            r = slot / per;
+        }
     } else {
         pair = id % BH;
         r = id / BH;
@@ -116,7 +124,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int g = lane >> 5;        // which half of the k-slots this lane supplies
 
     int pair, qt;
-    map_work(blockIdx.x, n_qt, BH, CAUSAL, pair, qt);
+    map_work(blockIdx.x, n_qt, BH, H / Hkv, CAUSAL, pair, qt);
     const int b = pair / H, h = pair % H;
     const int kvh = h / (H / Hkv);
     const int q0 = qt * T::BM;
