@@ -31,6 +31,19 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t b
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane L writes lds_base + 16 L
+// (buffer_load_dwordx4 ... lds). lds_base must be the same in all lanes; loads past the
+// descriptor's size write zeros. The builtin only exists for the device, and naming it
+// in a kernel template's host-side instantiation drops the kernel's launch stub, so it
+// lives behind this device-only wrapper.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_base,
+                                               uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff, 0, 0);
+#endif
+}
+
 // ---- bf16 <-> fp32 --------------------------------------------------------------
 // Low / high bf16 of a packed dword, widened exactly.
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }

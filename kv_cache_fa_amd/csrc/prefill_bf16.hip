@@ -57,18 +57,26 @@ struct Tile {
     static constexpr int KS = D / 16;           // MFMA k-steps of Q.K (16 dims each)
     static constexpr int DB = D / 32;           // 32-dim blocks of O^T
     static constexpr int PS = BN / 16;          // MFMA k-steps of P.V (16 keys each)
-    // Row pitches (bytes). K rows are padded by one 16-byte unit so the 16 rows read by a
-    // 16-lane group fall in 16 different bank groups; V rows are padded so the four rows
-    // gathered by one transposing read land 64 bytes apart in the bank space.
-    static constexpr int K_PITCH = D * 2 + 16;
-    static constexpr int V_PITCH = D * 2 + 64;
-    static constexpr int K_BYTES = BN * K_PITCH;
-    static constexpr int V_BYTES = BN * V_PITCH;
-    static constexpr int STAGE = K_BYTES + V_BYTES;
-    static constexpr int LD = BN * CH / NT;     // 16-byte chunks per thread per tile, each of K, V
-    static_assert((K_PITCH / 16) % 2 == 1, "odd K pitch in 16-byte units");
-    static_assert((V_PITCH / 16) % 16 == 4 || (V_PITCH / 16) % 16 == 12, "V pitch = 4 (mod 16) units");
+    static constexpr int ROW = D * 2;           // bytes per K/V row (rows are unpadded)
+    static constexpr int TILE = BN * ROW;       // bytes of one K (or V) tile
+    static constexpr int DMA = TILE / 1024 / (NT / 64);  // 1 KiB direct loads per wave per tile
+    static_assert(DMA >= 1 && DMA * 1024 * (NT / 64) == TILE, "whole 1 KiB loads per wave");
 };
+
+// XOR swizzles of the 16-byte chunks of a tile row (a direct-to-LDS load writes 1 KiB
+// contiguously, so rows cannot be padded). K: the 16 rows read together by a 16-lane
+// group for one MFMA operand land on 16 different bank groups. V: the 4 rows gathered by
+// one transposing read land on 4 different 64-byte bank groups.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+    if constexpr (D == 128) return row & 15;
+    else return (row >> 1) & 7;
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+    if constexpr (D == 128) return 4 * (row & 3);
+    else return 4 * ((row >> 1) & 1);
+}
 
 // Work-group id -> (batch*H + head, q tile). The dispatcher places work-group i on XCD
 // i % 8, and each XCD has its own L2. When the (batch, head) count is a multiple of 8,
@@ -108,6 +116,14 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
     return __builtin_bit_cast(u32x2, v);
 }
 
+// Per-iteration schedule of one wave (tile j):
+//   issue S_{j+1} = K_{j+1} Q^T on MFMA  |  softmax of S_j on the VALU (mask, running max,
+//   rescale, P_j = exp2(...)), then O^T += V_j^T P_j^T on MFMA
+// so the MFMAs of the next tile's scores overlap this tile's softmax inside each wave.
+// Tiles go from HBM straight into LDS (buffer_load ... lds): K two tiles ahead and V one
+// tile ahead, each into one of two stages that are separate LDS arrays, so the compiler
+// can tell that the loads in flight never alias the stage being read; the work-group
+// barrier that ends tile j (after the loads complete) publishes K_{j+2} and V_{j+1}.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -116,10 +132,14 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                      int BH, float scale_log2, float tau_raw) {
     using T = Tile<D>;
     constexpr int BN = T::BN;
-    __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
+    __shared__ __attribute__((aligned(1024))) char ks0[T::TILE];
+    __shared__ __attribute__((aligned(1024))) char ks1[T::TILE];
+    __shared__ __attribute__((aligned(1024))) char vs0[T::TILE];
+    __shared__ __attribute__((aligned(1024))) char vs1[T::TILE];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
     const int col = lane & 31;      // query column of S^T / O^T owned by this lane
     const int g = lane >> 5;        // which half of the k-slots this lane supplies
 
@@ -150,66 +170,67 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         full = min(full, (q0 + off + 1) / BN);
     }
 
-    // Per-lane LDS byte offsets (stage-relative); every other term is an immediate.
-    const int k_lane = col * T::K_PITCH + g * 16;
-    const int vG = lane >> 4, vj = lane & 15;
-    const int v_lane = T::K_BYTES + ((vG >> 1) * 4 + (vj >> 2)) * T::V_PITCH + 32 * (vG & 1) +
-                       8 * (vj & 3);
-
-    // Global -> register staging of one K/V tile (rows past Nk load as zero).
-    u32x4 kr[T::LD], vr[T::LD];
-    auto load_tile = [&](int j) {
-        const int kb0 = j * BN;
+    // Direct loads: the wave's i-th 1 KiB piece of a tile covers tile bytes
+    // [1024 (DMA w + i), +1024); lane L fills byte 16 L of it, i.e. row r, physical chunk
+    // pc, with logical chunk pc ^ swizzle(r) of row r.
+    uint32_t dk_off[T::DMA], dv_off[T::DMA];
 #pragma unroll
-        for (int i = 0; i < T::LD; ++i) {
-            const int e = tid + T::NT * i, row = e / T::CH, c = e % T::CH;
-            const uint32_t go = (uint32_t)((kb0 + row) * D + c * 8) * 2;
-            kr[i] = buf_load16(rk, go);
-            vr[i] = buf_load16(rv, go);
-        }
+    for (int i = 0; i < T::DMA; ++i) {
+        const int byte = 1024 * (T::DMA * w + i) + 16 * lane;
+        const int r = byte / T::ROW, pc = (byte % T::ROW) / 16;
+        dk_off[i] = (uint32_t)(r * T::ROW + ((pc ^ k_swz<D>(r)) * 16));
+        dv_off[i] = (uint32_t)(r * T::ROW + ((pc ^ v_swz<D>(r)) * 16));
+    }
+    auto load_k = [&](int j, char* dst) {
+#pragma unroll
+        for (int i = 0; i < T::DMA; ++i)
+            buf_load16_lds(rk, dst + 1024 * (T::DMA * w + i), dk_off[i], (uint32_t)(j * T::TILE));
     };
-    auto store_tile = [&](int stage) {
-        char* ks = smem + stage * T::STAGE;
-        char* vs = ks + T::K_BYTES;
+    auto load_v = [&](int j, char* dst) {
 #pragma unroll
-        for (int i = 0; i < T::LD; ++i) {
-            const int e = tid + T::NT * i, row = e / T::CH, c = e % T::CH;
-            *reinterpret_cast<u32x4*>(ks + row * T::K_PITCH + c * 16) = kr[i];
-            *reinterpret_cast<u32x4*>(vs + row * T::V_PITCH + c * 16) = vr[i];
-        }
+        for (int i = 0; i < T::DMA; ++i)
+            buf_load16_lds(rv, dst + 1024 * (T::DMA * w + i), dv_off[i], (uint32_t)(j * T::TILE));
     };
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    // Per-lane LDS read offsets. K operand (kb, s): row 32 kb + col, logical chunk 2s + g.
+    // V^T operand (t, db, half): rows 16t + 8 half + 4(G/2) + e, logical chunk
+    // 4 db + 2(G%2) + a/2, byte 8(a%2) in it (G = lane/16, lane%16 = a + 4e).
+    int kr_off[T::KS];
+#pragma unroll
+    for (int s = 0; s < T::KS; ++s)
+        kr_off[s] = col * T::ROW + (((2 * s + g) ^ k_swz<D>(col)) * 16);
+    const int vG = lane >> 4, va = lane & 3, ve = (lane >> 2) & 3;
+    const int vrow = (vG >> 1) * 4 + ve;  // row within a 16-key step (swizzle depends on it only)
+    int vr_off[T::DB];
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+        vr_off[db] = vrow * T::ROW + (((4 * db + 2 * (vG & 1) + (va >> 1)) ^ v_swz<D>(vrow)) * 16) +
+                     8 * (va & 1);
 
     float m_used = -INFINITY;  // raw-score reference max of this lane's query
     float l_part = 0.f;        // this lane's share of the row sum
     f32x16 oacc[T::DB];
 #pragma unroll
     for (int i = 0; i < T::DB; ++i) oacc[i] = f32x16{};
+    // Score accumulators of two consecutive tiles; which one is current alternates with
+    // the tile's parity, a compile-time constant at every call site.
+    f32x16 sbuf[2][T::KB];
 
-    // One K/V tile: scores, (mask), online softmax, P.V, then stage the prefetched tile.
-    auto tile = [&](const int j, auto masked) {
-        const int cur = j & 1;
-        if (j + 1 < n_tiles) load_tile(j + 1);
-        const char* kl = smem + cur * T::STAGE + k_lane;
-        const char* vl = smem + cur * T::STAGE + v_lane;
-
-        // ---- S^T = K Q^T for this tile ----
-        f32x16 sacc[T::KB];
+    auto scores = [&](const char* kst, auto par) {
+        f32x16 (&sacc)[T::KB] = sbuf[decltype(par)::value];
 #pragma unroll
         for (int kb = 0; kb < T::KB; ++kb) {
             sacc[kb] = f32x16{};
 #pragma unroll
             for (int s = 0; s < T::KS; ++s) {
-                const u32x4 a =
-                    *reinterpret_cast<const u32x4*>(kl + kb * 32 * T::K_PITCH + s * 32);
+                const u32x4 a = *reinterpret_cast<const u32x4*>(kst + kr_off[s] + kb * 32 * T::ROW);
                 sacc[kb] = mfma32x32x16(a, qf[s], sacc[kb]);
             }
         }
+    };
 
-        // ---- mask (diagonal / ragged tiles only) ----
+    auto softmax_pv = [&](const int j, const char* vst, auto par, auto masked) {
+        f32x16 (&sacc)[T::KB] = sbuf[decltype(par)::value];
         if constexpr (decltype(masked)::value) {
             // key offset inside the tile of element (kb, i) is kb*32 + 8*(i/4) + 4g + i%4;
             // it is dead past the row's last key and past Nk.
@@ -221,7 +242,6 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 for (int i = 0; i < 16; ++i)
                     if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sacc[kb][i] = -INFINITY;
         }
-        // ---- online softmax ----
         // Every row attends key 0 (causal rows see the whole prefix), so after the
         // first tile the max is finite and no -inf - -inf can occur.
         float mx = sacc[0][0];
@@ -246,40 +266,66 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         }
         const float mb = m_used * scale_log2;
 #pragma unroll
-        for (int kb = 0; kb < T::KB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -mb));
-                l_part += p;
-                sacc[kb][i] = p;
-            }
-
-        // ---- O^T += V^T P^T ----
-#pragma unroll
         for (int t = 0; t < T::PS; ++t) {
             const int kb = t >> 1, base = (t & 1) * 8;
             u32x4 pf;
-            pf[0] = pack_bf16x2(sacc[kb][base + 0], sacc[kb][base + 1]);
-            pf[1] = pack_bf16x2(sacc[kb][base + 2], sacc[kb][base + 3]);
-            pf[2] = pack_bf16x2(sacc[kb][base + 4], sacc[kb][base + 5]);
-            pf[3] = pack_bf16x2(sacc[kb][base + 6], sacc[kb][base + 7]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float p0 = fast_exp2(fmaf(sacc[kb][base + 2 * u], scale_log2, -mb));
+                const float p1 = fast_exp2(fmaf(sacc[kb][base + 2 * u + 1], scale_log2, -mb));
+                pf[u] = pack_bf16x2(p0, p1);
+                l_part += p0 + p1;  // fp32 sum of the unrounded exponentials
+            }
 #pragma unroll
             for (int db = 0; db < T::DB; ++db) {
                 // keys 16t + 4g + {0..3} and 16t + 8 + 4g + {0..3} at dim 32db + col
-                const u32x2 a0 = lds_read_tr(vl + (t * 16) * T::V_PITCH + 64 * db);
-                const u32x2 a1 = lds_read_tr(vl + (t * 16 + 8) * T::V_PITCH + 64 * db);
+                const u32x2 a0 = lds_read_tr(vst + vr_off[db] + (t * 16) * T::ROW);
+                const u32x2 a1 = lds_read_tr(vst + vr_off[db] + (t * 16 + 8) * T::ROW);
                 const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
                 oacc[db] = mfma32x32x16(a, pf, oacc[db]);
             }
         }
-
-        if (j + 1 < n_tiles) store_tile(cur ^ 1);
-        __syncthreads();
     };
 
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    // Tile j with stage parity par = j & 1: K_j and V_j are in ks<par>, vs<par>.
+    auto step = [&](const int j, auto par, auto masked) {
+        constexpr int pv = decltype(par)::value;
+        using Next = std::integral_constant<int, 1 - pv>;
+        char* k_cur = pv ? ks1 : ks0;   // K_j: its stage receives K_{j+2}
+        char* k_nxt = pv ? ks0 : ks1;   // K_{j+1}
+        char* v_cur = pv ? vs1 : vs0;   // V_j
+        char* v_nxt = pv ? vs0 : vs1;   // receives V_{j+1}
+        if (j + 2 < n_tiles) load_k(j + 2, k_cur);
+        if (j + 1 < n_tiles) {
+            load_v(j + 1, v_nxt);
+            scores(k_nxt, Next{});
+        }
+        softmax_pv(j, v_cur, par, masked);
+        __syncthreads();  // completes the loads above and publishes K_{j+2}, V_{j+1}
+    };
+
+    // Prologue: K_0, V_0, K_1 in place; S_0 computed; a barrier separates the S_0 reads
+    // from step 0's load into K_0's stage.
+    load_k(0, ks0);
+    load_v(0, vs0);
+    if (n_tiles > 1) load_k(1, ks1);
+    __syncthreads();
+    scores(ks0, P0{});
+    __syncthreads();
+
+    // Unmasked tiles two at a time (stage parity alternates), then the rest with masking.
     const int n_plain = min(full, n_tiles);
-    for (int j = 0; j < n_plain; ++j) tile(j, std::false_type{});
-    for (int j = n_plain; j < n_tiles; ++j) tile(j, std::true_type{});
+    int j = 0;
+    for (; j + 1 < n_plain; j += 2) {
+        step(j, P0{}, std::false_type{});
+        step(j + 1, P1{}, std::false_type{});
+    }
+    for (; j < n_tiles; j += 2) {
+        step(j, P0{}, std::true_type{});
+        if (j + 1 < n_tiles) step(j + 1, P1{}, std::true_type{});
+    }
 
     // ---- epilogue: O = O_acc / l, lse = M + ln L ----
     const float l = l_part + xor32(l_part);
