@@ -227,6 +227,14 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 sacc[kb] = mfma32x32x16(a, qf[s], sacc[kb]);
             }
         }
+        // Schedule: each K operand read goes three MFMAs ahead of its use.
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS reads
+#pragma unroll
+        for (int i = 0; i < T::KB * T::KS - 3; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     };
 
     auto softmax_pv = [&](const int j, const char* vst, auto par, auto masked) {
@@ -285,6 +293,14 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 oacc[db] = mfma32x32x16(a, pf, oacc[db]);
             }
         }
+        // Schedule: the V^T operand reads go two MFMAs ahead of their use.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < T::PS * T::DB - 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     };
 
     using P0 = std::integral_constant<int, 0>;
