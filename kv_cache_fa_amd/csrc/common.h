@@ -31,6 +31,12 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t b
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }
 
+// The same with the nontemporal hint (the `nt` bit; cache-policy argument 2 on gfx950),
+// for data that is streamed once.
+__device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2);
+}
+
 // 16 bytes per lane from a buffer straight into LDS: lane L writes lds_base + 16 L
 // (buffer_load_dwordx4 ... lds). lds_base must be the same in all lanes; loads past the
 // descriptor's size write zeros. The builtin only exists for the device, and naming it

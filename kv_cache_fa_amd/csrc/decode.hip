@@ -98,6 +98,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     // the P.V lanes). Returns false for an out-of-range page id, which is never read.
     // Loads are issued unconditionally (a zero-size descriptor for an invalid page id
     // makes them return zeros without touching memory), so the wait counts stay exact.
+    // The cache is read once per call: the loads carry the nontemporal hint.
     const uint32_t span = (uint32_t)((kPage - 1) * tok_stride + D) * 2;
     const uint32_t k_off = (uint32_t)(n * tok_stride) * 2 + kq * 16;
     const uint32_t v_off = (uint32_t)(tg * tok_stride + c * 8) * 2;
@@ -108,9 +109,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         const auto rk = make_rsrc(kcache + page_base, valid ? span : 0u);
         const auto rv = make_rsrc(vcache + page_base, valid ? span : 0u);
 #pragma unroll
-        for (int j = 0; j < KS; ++j) kf[j] = buf_load16(rk, k_off + j * 64);
+        for (int j = 0; j < KS; ++j) kf[j] = buf_load16_nt(rk, k_off + j * 64);
 #pragma unroll
-        for (int i = 0; i < TPL; ++i) vv[i] = buf_load16(rv, v_off + (uint32_t)(TG * i * tok_stride) * 2);
+        for (int i = 0; i < TPL; ++i)
+            vv[i] = buf_load16_nt(rv, v_off + (uint32_t)(TG * i * tok_stride) * 2);
         return valid;
     };
 
@@ -233,15 +235,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     }
 }
 
-// Merge the splits of one (sequence, head): LSE = log2 sum_k 2^lse_k (relative to the
-// largest), O = sum_k 2^(lse_k - LSE) O_k. One wave per (sequence, head).
+// Merge the splits of each (sequence, head): LSE = log2 sum_k 2^lse_k (relative to the
+// largest), O = sum_k 2^(lse_k - LSE) O_k. A work-group of 256 threads takes one
+// sequence and kCombineHeads consecutive heads; a head's D outputs are spread over
+// D / kCombinePer threads, so every split's partial row is read with consecutive lanes.
+constexpr int kCombineHeads = 4;
 template <int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(
+__global__ __launch_bounds__(256) void decode_combine_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part,
     const int32_t* __restrict__ seq_lens, uint16_t* __restrict__ o, float* __restrict__ lse,
     int H, int max_seq_len, int split_tokens, int max_splits) {
-    constexpr int PER = D / 64;  // output dims per lane
-    const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+    constexpr int TPH = 256 / kCombineHeads;  // threads per head
+    constexpr int PER = D / TPH;              // output dims per thread (2 or 1)
+    const int s = blockIdx.y, tid = threadIdx.x;
+    const int h = blockIdx.x * kCombineHeads + tid / TPH;
+    const int lt = tid % TPH;
+    if (h >= H) return;
     const int L = min(max(seq_lens[s], 0), max_seq_len);
     const int ns = (L + split_tokens - 1) / split_tokens;
     const size_t row = (size_t)s * H + h;
@@ -257,21 +266,26 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
         for (int kk = 0; kk < ns; ++kk) {
             const float f = fast_exp2(lp[kk] - M);
             W += f;
-            const float* op = o_part + (row * max_splits + kk) * D + lane * PER;
-#pragma unroll
-            for (int e = 0; e < PER; ++e) out[e] = fmaf(f, op[e], out[e]);
+            const float* op = o_part + (row * max_splits + kk) * D + lt * PER;
+            if constexpr (PER == 2) {
+                const f32x2 x = *reinterpret_cast<const f32x2*>(op);
+                out[0] = fmaf(f, x[0], out[0]);
+                out[1] = fmaf(f, x[1], out[1]);
+            } else {
+                out[0] = fmaf(f, op[0], out[0]);
+            }
         }
         const float inv = 1.f / W;
 #pragma unroll
         for (int e = 0; e < PER; ++e) out[e] *= inv;
     }
-    uint16_t* orow = o + row * D + lane * PER;
+    uint16_t* orow = o + row * D + lt * PER;
     if constexpr (PER == 2) {
         *reinterpret_cast<uint32_t*>(orow) = pack_bf16x2(out[0], out[1]);
     } else {
         orow[0] = (uint16_t)(pack_bf16x2(out[0], 0.f) & 0xffffu);
     }
-    if (lse != nullptr && lane == 0)
+    if (lse != nullptr && lt == 0)
         lse[row] = M != -INFINITY ? (M + fast_log2(W)) * kLn2 : -INFINITY;
 }
 
@@ -355,13 +369,13 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
                              num_seqs, H, Hkv, g, n_hg, num_pages, max_pages_per_seq,
                              max_seq_len, T, max_splits, scale, stream);
     if (e != hipSuccess) return e;
-    dim3 grid(H, num_seqs);
+    dim3 grid((H + kCombineHeads - 1) / kCombineHeads, num_seqs);
     if (d == 128)
-        hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(64), 0, stream, o_part,
+        hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(256), 0, stream, o_part,
                            lse_part, seq_lens, static_cast<uint16_t*>(o), lse, H, max_seq_len, T,
                            max_splits);
     else
-        hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(64), 0, stream, o_part,
+        hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(256), 0, stream, o_part,
                            lse_part, seq_lens, static_cast<uint16_t*>(o), lse, H, max_seq_len, T,
                            max_splits);
     return hipGetLastError();
