@@ -108,6 +108,57 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  * size); the workspace holds ceil(max_seq_len / split) partial results per head. */
 int fa_decode_paged_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size);
 
+/*
+ * fa_fwd_paged — chunked prefill: bf16 attention of Nq new queries per sequence against
+ * all of that sequence's cached keys, read through the page table (the prompt is fed
+ * in chunks, each chunk's K/V first appended with fa_kv_append; glossary entry "KV
+ * Cache (Anahtar-Değer Önbelleği)": later tokens read the stored K/V of earlier ones).
+ *   q          [B, H, Nq, d] bf16          o [B, H, Nq, d] bf16 (written)
+ *   k_cache,   [num_pages, page_size, Hkv, d] bf16, the layout of fa_decode_paged
+ *   v_cache
+ *   page_table [B, max_pages_per_seq] int32
+ *   seq_lens   [B] int32, device memory: cached tokens of each sequence INCLUDING the
+ *              Nq new ones, which are its last Nq tokens (query i sits at position
+ *              seq_len - Nq + i; causal masking is bottom-right as everywhere)
+ *   lse        [B, H, Nq] fp32 (written; may be NULL)
+ * Numerics as fa_fwd. Requirements: page_size == 16, d in {64, 128} (else
+ * FA_ERR_UNSUPPORTED); B, H, Hkv, Nq, num_pages >= 1; H % Hkv == 0;
+ * Nq <= max_seq_len <= max_pages_per_seq * page_size; Nq * d * 2 < 2^31.
+ * Device-side values: a seq_len outside [Nq, max_seq_len] is clamped into it; pages
+ * with ids outside [0, num_pages) load as zeros (the result is then not meaningful);
+ * table entries past a sequence's last page and slots past its length are never read.
+ */
+int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* page_table, const int32_t* seq_lens, int page_size, void* o,
+                 float* lse, int B, int H, int Hkv, int Nq, int d, int num_pages,
+                 int max_pages_per_seq, int max_seq_len, int causal, float scale,
+                 void* stream);
+
+/*
+ * fa_kv_append — store the keys and values of n_new new tokens per sequence in the
+ * paged cache (glossary entry "KV Cache (Anahtar-Değer Önbelleği)": each token's K/V
+ * is computed once and kept for every later step). A bit-exact copy, no arithmetic.
+ *   k_new, v_new [num_seqs, n_new, Hkv, d] bf16 (read)
+ *   k_cache,     [num_pages, page_size, Hkv, d] bf16 (the new slots are written)
+ *   v_cache
+ *   page_table   [num_seqs, max_pages_per_seq] int32; the pages that will hold the new
+ *                tokens must already be assigned by the caller
+ *   start_pos    [num_seqs] int32, device memory: position of the first new token of
+ *                each sequence (its cached length before the call)
+ * Token t of sequence s goes to slot (start_pos[s] + t) % page_size of page
+ * page_table[s][(start_pos[s] + t) / page_size].
+ * Requirements: page_size == 16, d in {64, 128} (else FA_ERR_UNSUPPORTED);
+ * num_seqs, n_new, Hkv, num_pages, max_pages_per_seq >= 1.
+ * Device-side values: a token whose position is negative or past the table
+ * (>= max_pages_per_seq * page_size), or whose page id is outside [0, num_pages), is
+ * not written. Two tokens mapped to the same slot (a table that shares a page being
+ * written) race; which one lands is unspecified.
+ */
+int fa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                 const int32_t* page_table, const int32_t* start_pos, int page_size,
+                 int num_seqs, int n_new, int Hkv, int d, int num_pages,
+                 int max_pages_per_seq, void* stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* fa_status_string(int status);
 

@@ -1,4 +1,5 @@
-"""Exact attention for AMD MI355X (gfx950): bf16/fp32 prefill and paged-KV decode.
+"""Exact attention for AMD MI355X (gfx950): bf16/fp32 prefill, paged-KV decode,
+chunked prefill through the page table and the KV append that fills it.
 
 The kernels are hand-written HIP in ``csrc/`` behind the C ABI of
 ``include/kvfa.h`` (``libkvfa.so``); ``kv_cache_fa_amd._lib`` is the ctypes binding
@@ -13,6 +14,8 @@ from ._lib import (  # noqa: F401
     fa_decode_paged_workspace_size,
     fa_fwd,
     fa_fwd_fp32,
+    fa_fwd_paged,
+    fa_kv_append,
     fa_status_string,
     lib,
 )

@@ -26,6 +26,9 @@ SIGNATURES = {
     "fa_decode_paged_split_tokens": (_i, [_i, _i, _i, _i]),
     "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                              _f, _vp, _sz, _vp]),
+    "fa_fwd_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                          _i, _f, _vp]),
+    "fa_kv_append": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
 }
 
@@ -155,3 +158,48 @@ def fa_decode_paged(q, k_cache, v_cache, page_table, seq_lens, o, lse=None, *, m
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), page_size,
         _ptr(o), _ptr(lse), S, H, Hkv, d, num_pages, int(page_table.shape[1]), int(max_seq_len),
         float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def fa_fwd_paged(q, k_cache, v_cache, page_table, seq_lens, o, lse=None, *, max_seq_len: int,
+                 causal: bool, scale: float, stream=None):
+    """Chunked prefill through the page table. q,o [B,H,Nq,d] bf16; caches [P,16,Hkv,d]
+    bf16; page_table [B,M] int32; seq_lens [B] int32 (device, new tokens included)."""
+    import torch
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (o, "o")):
+        _check_tensor(t, torch.bfloat16, n)
+    _check_tensor(page_table, torch.int32, "page_table")
+    _check_tensor(seq_lens, torch.int32, "seq_lens")
+    B, H, Nq, d = q.shape
+    num_pages, page_size, Hkv, dk = k_cache.shape
+    _require(dk == d and tuple(v_cache.shape) == tuple(k_cache.shape), "cache shape mismatch")
+    _require(tuple(o.shape) == tuple(q.shape), "o must have q's shape")
+    _require(page_table.dim() == 2 and page_table.shape[0] == B, "page_table must be [B, M]")
+    _require(tuple(seq_lens.shape) == (B,), "seq_lens must be [B]")
+    if lse is not None:
+        _check_tensor(lse, torch.float32, "lse")
+        _require(tuple(lse.shape) == (B, H, Nq), "lse must be [B,H,Nq]")
+    _check("fa_fwd_paged", lib().fa_fwd_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), page_size,
+        _ptr(o), _ptr(lse), B, H, Hkv, Nq, d, num_pages, int(page_table.shape[1]),
+        int(max_seq_len), int(bool(causal)), float(scale), _stream(stream)))
+
+
+def fa_kv_append(k_new, v_new, k_cache, v_cache, page_table, start_pos, *, stream=None):
+    """Scatter new tokens' K/V into the paged cache. k_new,v_new [S,n_new,Hkv,d] bf16;
+    caches [P,16,Hkv,d] bf16; page_table [S,M] int32; start_pos [S] int32 (device)."""
+    import torch
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _check_tensor(t, torch.bfloat16, n)
+    _check_tensor(page_table, torch.int32, "page_table")
+    _check_tensor(start_pos, torch.int32, "start_pos")
+    S, n_new, Hkv, d = k_new.shape
+    num_pages, page_size, Hkv_c, dk = k_cache.shape
+    _require(tuple(v_new.shape) == tuple(k_new.shape), "k_new/v_new shape mismatch")
+    _require(Hkv_c == Hkv and dk == d and tuple(v_cache.shape) == tuple(k_cache.shape),
+             "cache shape mismatch")
+    _require(page_table.dim() == 2 and page_table.shape[0] == S, "page_table must be [S, M]")
+    _require(tuple(start_pos.shape) == (S,), "start_pos must be [S]")
+    _check("fa_kv_append", lib().fa_kv_append(
+        _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+        _ptr(start_pos), page_size, S, n_new, Hkv, d, num_pages, int(page_table.shape[1]),
+        _stream(stream)))

@@ -101,6 +101,51 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* page_table, const int32_t* seq_lens, int page_size, void* o,
+                 float* lse, int B, int H, int Hkv, int Nq, int d, int num_pages,
+                 int max_pages_per_seq, int max_seq_len, int causal, float scale,
+                 void* stream) {
+    if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !o) return FA_ERR_INVALID;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+        !aligned(page_table, 4) || !aligned(seq_lens, 4))
+        return FA_ERR_INVALID;
+    if (lse && !aligned(lse, 4)) return FA_ERR_INVALID;
+    if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || num_pages < 1 || max_pages_per_seq < 1)
+        return FA_ERR_INVALID;
+    if (H % Hkv != 0) return FA_ERR_INVALID;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID;
+    if (page_size != 16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+    if (max_seq_len < Nq || (long long)max_pages_per_seq * page_size < max_seq_len)
+        return FA_ERR_INVALID;
+    if ((unsigned long long)Nq * d * 2 >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+    const unsigned long long n_wg = (unsigned long long)((Nq + 127) / 128) * B * H;
+    if (n_wg >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+    hipError_t e = kvfa::launch_fwd_bf16_paged(q, k_cache, v_cache, page_table, seq_lens, o, lse,
+                                               B, H, Hkv, Nq, d, num_pages, max_pages_per_seq,
+                                               max_seq_len, causal != 0, scale,
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                 const int32_t* page_table, const int32_t* start_pos, int page_size,
+                 int num_seqs, int n_new, int Hkv, int d, int num_pages,
+                 int max_pages_per_seq, void* stream) {
+    if (!k_new || !v_new || !k_cache || !v_cache || !page_table || !start_pos)
+        return FA_ERR_INVALID;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+        !aligned(v_cache, 16) || !aligned(page_table, 4) || !aligned(start_pos, 4))
+        return FA_ERR_INVALID;
+    if (num_seqs < 1 || n_new < 1 || Hkv < 1 || num_pages < 1 || max_pages_per_seq < 1)
+        return FA_ERR_INVALID;
+    if (page_size != 16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+    hipError_t e = kvfa::launch_kv_append(k_new, v_new, k_cache, v_cache, page_table, start_pos,
+                                          num_seqs, n_new, Hkv, d, num_pages, max_pages_per_seq,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "FA_OK";

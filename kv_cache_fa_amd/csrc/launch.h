@@ -17,6 +17,17 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                            hipStream_t stream);
 
+hipError_t launch_fwd_bf16_paged(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* page_table, const int32_t* seq_lens, void* o,
+                                 float* lse, int B, int H, int Hkv, int Nq, int d, int num_pages,
+                                 int max_pages_per_seq, int max_seq_len, int causal, float scale,
+                                 hipStream_t stream);
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            const int32_t* page_table, const int32_t* start_pos, int num_seqs,
+                            int n_new, int Hkv, int d, int num_pages, int max_pages_per_seq,
+                            hipStream_t stream);
+
 // Decode split plan: tokens per split-K work-group, and the workspace it implies.
 int decode_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size);
 size_t decode_workspace_bytes(int num_seqs, int H, int Hkv, int d, int max_seq_len,

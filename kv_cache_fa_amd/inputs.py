@@ -298,3 +298,64 @@ def custom_decode(num_seqs, H, Hkv, d, len_lo, len_hi, page_size=16, max_seq_len
     cfg = DecodeConfig("custom_decode", num_seqs, H, Hkv, d, len_lo, len_hi, page_size,
                        max_seq_len, scale, seed)
     return make_decode(cfg, **kw)
+
+
+# ----------------------------------------------------------------------------------
+# Chunked prefill through the page table, and KV append
+# ----------------------------------------------------------------------------------
+@dataclasses.dataclass
+class ChunkedPrefillInputs:
+    cache: DecodeInputs   # the paged cache; seq_lens include the Nq new tokens
+    q: np.ndarray         # [B,H,Nq,d] uint16 bf16 bits: queries of each sequence's last Nq tokens
+    Nq: int
+
+
+def custom_chunked_prefill(B, H, Hkv, d, Nq, len_lo, len_hi, *, seq_lens=None,
+                           max_seq_len=None, scale=None, seed=0, **kw) -> ChunkedPrefillInputs:
+    """A paged cache of B sequences (lengths U{len_lo..len_hi}, each >= Nq, or
+    ``seq_lens``) plus queries for the last Nq tokens of each sequence."""
+    assert len_lo >= Nq or seq_lens is not None
+    if max_seq_len is None:
+        max_seq_len = max(len_hi, int(max(seq_lens)) if seq_lens is not None else 1)
+    cache = custom_decode(B, H, Hkv, d, len_lo, len_hi, max_seq_len=max_seq_len, scale=scale,
+                          seed=seed, seq_lens=seq_lens, **kw)
+    rng = np.random.default_rng(seed + 7919)
+    q = _draw(rng, (B, H, Nq, d), 1.0, "bf16")
+    return ChunkedPrefillInputs(cache, q, Nq)
+
+
+@dataclasses.dataclass
+class AppendInputs:
+    k_cache: np.ndarray    # [num_pages,16,Hkv,d] uint16, random "old" contents
+    v_cache: np.ndarray
+    page_table: np.ndarray  # [S,max_pages] int32: disjoint pages; unassigned entries -1
+    start_pos: np.ndarray   # [S] int32
+    k_new: np.ndarray      # [S,n_new,Hkv,d] uint16
+    v_new: np.ndarray
+
+
+def make_append(S, n_new, Hkv, d, max_seq_len, *, page_size=16, seed=0, start_pos=None,
+                spare_pages=3) -> AppendInputs:
+    """Seeded KV-append workload: sequence s already holds start_pos[s] tokens (drawn
+    in [0, max_seq_len - n_new] unless given) and gets n_new more. Its pages up to
+    the last new token are assigned (a seeded permutation of the pool, which has
+    ``spare_pages`` pages nobody owns); later table entries hold -1."""
+    rng = np.random.default_rng(seed)
+    P = page_size
+    max_pages = (max_seq_len + P - 1) // P
+    if start_pos is None:
+        start_pos = rng.integers(0, max(max_seq_len - n_new, 0), size=S, endpoint=True)
+    start_pos = np.asarray(start_pos, dtype=np.int32)
+    need = np.clip((start_pos.astype(np.int64) + n_new + P - 1) // P, 0, max_pages)
+    total = int(need.sum()) + spare_pages
+    perm = rng.permutation(total).astype(np.int32)
+    table = np.full((S, max_pages), -1, dtype=np.int32)
+    off = 0
+    for s in range(S):
+        table[s, :need[s]] = perm[off:off + need[s]]
+        off += int(need[s])
+    k_cache = rng.integers(0, 1 << 16, size=(total, P, Hkv, d), dtype=np.uint16)
+    v_cache = rng.integers(0, 1 << 16, size=(total, P, Hkv, d), dtype=np.uint16)
+    k_new = _draw(rng, (S, n_new, Hkv, d), 1.0, "bf16")
+    v_new = _draw(rng, (S, n_new, Hkv, d), 1.0, "bf16")
+    return AppendInputs(k_cache, v_cache, table, start_pos, k_new, v_new)

@@ -16,5 +16,6 @@ from .attention import (  # noqa: F401
     merge_partials,
     online_attention_row,
     online_softmax_stats,
+    scatter_pages,
     softmax_rows,
 )

@@ -26,7 +26,8 @@ Sources (the pages; translations are mine):
   result equals standard attention exactly (FAQ "does it change the output").
 * Same glossary page, entry "KV Cache (Anahtar-Değer Önbelleği)": token n+1 reads
   the cached K/V of the earlier tokens and its own K/V is appended; GQA/MQA give
-  one K-V head to several query heads; paged caches keep K/V in fixed-size pages.
+  one K-V head to several query heads; paged caches keep K/V in fixed-size pages
+  (``gather_pages`` reads them back, ``scatter_pages`` appends new tokens).
 
 Readings where the pages are silent (each also listed in the design notes):
 * causal alignment is bottom-right: query i sits at absolute position Nk-Nq+i and
@@ -157,6 +158,33 @@ def gather_pages(cache: np.ndarray, page_table: np.ndarray, seq_lens, page_size:
     for s, L in enumerate(np.asarray(seq_lens)):
         t = np.arange(int(L))
         out.append(cache[page_table[s, t // page_size], t % page_size])
+    return out
+
+
+def scatter_pages(cache: np.ndarray, page_table: np.ndarray, start_pos, new: np.ndarray,
+                  page_size: int) -> np.ndarray:
+    """Append new tokens to a paged cache; returns the updated copy (pure indexing).
+
+    Glossary entry "KV Cache (Anahtar-Değer Önbelleği)": each token's K (or V) is
+    stored once in the cache, after the tokens already there. new: [S, n_new, Hkv, d];
+    token t of sequence s is position p = start_pos[s] + t, which lives in slot
+    p % page_size of physical page page_table[s, p // page_size]. A token whose
+    position is negative or past the table, or whose page id is outside
+    [0, num_pages), is not stored. One token at a time, in order.
+    """
+    out = cache.copy()
+    num_pages = cache.shape[0]
+    S, n_new = new.shape[0], new.shape[1]
+    max_pages = page_table.shape[1]
+    for s in range(S):
+        for t in range(n_new):
+            p = int(start_pos[s]) + t
+            if p < 0 or p >= max_pages * page_size:
+                continue
+            pid = int(page_table[s, p // page_size])
+            if not 0 <= pid < num_pages:
+                continue
+            out[pid, p % page_size] = new[s, t]
     return out
 
 

@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert set(declared_functions()) == {
         "fa_fwd", "fa_fwd_fp32", "fa_decode_paged", "fa_decode_paged_workspace_size",
-        "fa_decode_paged_split_tokens", "fa_status_string"}
+        "fa_decode_paged_split_tokens", "fa_fwd_paged", "fa_kv_append", "fa_status_string"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -93,6 +93,45 @@ def _dec(lib, q=P, kc=P, vc=P, pt=P, sl=P, page_size=16, o=P, lse=None, S=4, H=3
 ])
 def test_decode_validation(lib, kw, want):
     assert _dec(lib, **kw) == want
+
+
+def _fwd_paged(lib, q=P, kc=P, vc=P, pt=P, sl=P, page_size=16, o=P, lse=None, B=2, H=16,
+               Hkv=4, Nq=100, d=128, num_pages=64, max_pages=16, max_seq_len=256, causal=1,
+               scale=0.09):
+    return lib.fa_fwd_paged(q, kc, vc, pt, sl, page_size, o, lse, B, H, Hkv, Nq, d, num_pages,
+                            max_pages, max_seq_len, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(kc=None), INVALID), (dict(pt=None), INVALID),
+    (dict(sl=None), INVALID), (dict(o=None), INVALID), (dict(vc=P + 8), INVALID),
+    (dict(sl=P + 2), INVALID), (dict(lse=P + 1), INVALID),
+    (dict(B=0), INVALID), (dict(Nq=0), INVALID), (dict(num_pages=0), INVALID),
+    (dict(max_pages=0), INVALID), (dict(H=16, Hkv=3), INVALID),
+    (dict(Nq=300, max_seq_len=256), INVALID),            # queries longer than any sequence
+    (dict(max_pages=15, max_seq_len=256), INVALID),      # table too short
+    (dict(scale=0.0), INVALID), (dict(scale=math.inf), INVALID),
+    (dict(page_size=8, max_pages=32), UNSUPPORTED), (dict(d=96), UNSUPPORTED),
+])
+def test_fwd_paged_validation(lib, kw, want):
+    assert _fwd_paged(lib, **kw) == want
+
+
+def _append(lib, kn=P, vn=P, kc=P, vc=P, pt=P, sp=P, page_size=16, S=4, n_new=8, Hkv=8,
+            d=128, num_pages=64, max_pages=16):
+    return lib.fa_kv_append(kn, vn, kc, vc, pt, sp, page_size, S, n_new, Hkv, d, num_pages,
+                            max_pages, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(kn=None), INVALID), (dict(vc=None), INVALID), (dict(pt=None), INVALID),
+    (dict(sp=None), INVALID), (dict(kn=P + 4), INVALID), (dict(sp=P + 2), INVALID),
+    (dict(S=0), INVALID), (dict(n_new=0), INVALID), (dict(Hkv=0), INVALID),
+    (dict(num_pages=0), INVALID), (dict(max_pages=0), INVALID),
+    (dict(page_size=32), UNSUPPORTED), (dict(d=80), UNSUPPORTED),
+])
+def test_kv_append_validation(lib, kw, want):
+    assert _append(lib, **kw) == want
 
 
 def test_workspace_size(lib):

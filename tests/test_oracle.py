@@ -177,6 +177,43 @@ def test_gather_pages_detects_a_wrong_slot():
     assert not np.array_equal(wrong, inp.k_seq[s])
 
 
+def test_scatter_pages_hand_worked():
+    """Hand-placed tokens (page size 4, one head, d = 1): seq 0 starts at position 3,
+    so its tokens go to page 2 slot 3 and page 0 slot 0; seq 1 at position 2 fills
+    page 1 slots 2-3; a third sequence's tokens hit an unassigned entry (-1) and then
+    run past the table, and are dropped."""
+    cache = np.zeros((3, 4, 1, 1))
+    table = np.array([[2, 0], [1, -1], [0, -1]], dtype=np.int32)
+    new = np.array([[10, 11], [20, 21], [30, 31]], dtype=np.float64).reshape(3, 2, 1, 1)
+    got = oracle.scatter_pages(cache, table, [3, 2, 7], new, 4)
+    want = np.array([[11, 0, 0, 0], [0, 0, 20, 21], [0, 0, 0, 10]], dtype=np.float64)
+    assert np.array_equal(got[:, :, 0, 0], want)
+    assert np.all(cache == 0)  # the input is not modified
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_scatter_then_gather_round_trip(seed):
+    """After appending, reading each sequence back through the table yields its old
+    tokens followed by the new ones; pages nobody owns are untouched."""
+    a = inputs.make_append(6, 37, 2, 16, 200, seed=seed)
+    P = 16
+    n_new = a.k_new.shape[1]
+    old_lens = a.start_pos
+    old = oracle.gather_pages(a.k_cache, a.page_table, old_lens, P)
+    got = oracle.scatter_pages(a.k_cache, a.page_table, a.start_pos, a.k_new, P)
+    back = oracle.gather_pages(got, a.page_table, old_lens + n_new, P)
+    for s in range(6):
+        assert np.array_equal(back[s][:old_lens[s]], old[s])
+        assert np.array_equal(back[s][old_lens[s]:], a.k_new[s])
+    owned = set(int(x) for x in a.page_table.ravel() if x >= 0)
+    for pid in range(a.k_cache.shape[0]):
+        if pid not in owned:
+            assert np.array_equal(got[pid], a.k_cache[pid])
+    # exactly n_new token rows changed per sequence (new values differ from old bits)
+    changed = np.any(got != a.k_cache, axis=(2, 3)).sum()
+    assert changed <= 6 * n_new
+
+
 def test_size_facts_from_the_pages():
     """The pages' printed sizes agree with the counting used for measurement."""
     facts = load_golden("size_facts.json")["facts"]
