@@ -254,6 +254,22 @@ def main(argv=None):
         "wall_s_timed": round(t_wall, 3),
     }
 
+    def timed(fn, n=20, warm_s=0.2):
+        """Mean ms of fn over n back-to-back launches, after ~warm_s of warm-up (the
+        clock ramps up under sustained load)."""
+        w0 = time.perf_counter()
+        while time.perf_counter() - w0 < warm_s:
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
     if not args.no_extra and args.prefill != "gqa_causal":
         gcfg = inputs.PREFILL_CONFIGS["gqa_causal"]
         log("[bench] extra: gqa_causal prefill")
@@ -261,27 +277,56 @@ def main(argv=None):
         gq, gk, gv = to_dev(ginp.q), to_dev(ginp.k), to_dev(ginp.v)
         go = torch.empty_like(gq)
         glse = torch.empty((gcfg.B, gcfg.H, gcfg.Nq), dtype=torch.float32, device=dev)
-        # warm up for ~0.2 s of GPU time: the clock ramps up under sustained load
-        w0 = time.perf_counter()
-        while time.perf_counter() - w0 < 0.2:
-            for _ in range(20):
-                _lib.fa_fwd(gq, gk, gv, go, glse, causal=True, scale=gcfg.scale, stream=stream)
-            torch.cuda.synchronize()
-        n = 20
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(n):
-            _lib.fa_fwd(gq, gk, gv, go, glse, causal=True, scale=gcfg.scale, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        g_ms = e0.elapsed_time(e1) / n
+        g_ms = timed(lambda: _lib.fa_fwd(gq, gk, gv, go, glse, causal=True, scale=gcfg.scale,
+                                         stream=stream))
         g_tf = gcfg.flops / (g_ms * 1e-3) / 1e12
         out["legs"]["prefill_gqa_causal"] = {
             "B": gcfg.B, "H": gcfg.H, "Hkv": gcfg.Hkv, "N": gcfg.Nq, "d": gcfg.d,
             "ms_mean": round(g_ms, 4), "TFLOP/s": round(g_tf, 2),
             "frac_of_bf16_peak": round(g_tf / PEAK_BF16_TFLOPS, 4)}
         del gq, gk, gv, go, glse
+
+    if not args.no_extra:
+        # Chunked prefill through the page table: a 1024-token chunk for each of 8
+        # sequences whose caches (chunk included) hold U{4096..16384} tokens.
+        B, H, Hkv, d, Nq = 8, 32, 8, 128, 1024
+        log("[bench] extra: chunked prefill through the page table")
+        ci = inputs.custom_chunked_prefill(B, H, Hkv, d, Nq, 4096, 16384, seed=1234)
+        c = ci.cache
+        cq, ckc, cvc = to_dev(ci.q), to_dev(c.k_cache), to_dev(c.v_cache)
+        cpt = torch.from_numpy(c.page_table).to(dev)
+        csl = torch.from_numpy(c.seq_lens).to(dev)
+        co = torch.empty_like(cq)
+        clse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+        c_ms = timed(lambda: _lib.fa_fwd_paged(cq, ckc, cvc, cpt, csl, co, clse,
+                                               max_seq_len=c.cfg.max_seq_len, causal=True,
+                                               scale=c.cfg.scale, stream=stream))
+        c_flops = sum(4.0 * d * H * inputs.unmasked_pairs(Nq, int(L), True)
+                      for L in c.seq_lens)
+        c_tf = c_flops / (c_ms * 1e-3) / 1e12
+        out["legs"]["chunked_prefill_paged"] = {
+            "B": B, "H": H, "Hkv": Hkv, "Nq": Nq, "d": d,
+            "seq_lens": [int(x) for x in c.seq_lens], "flops": c_flops,
+            "ms_mean": round(c_ms, 4), "TFLOP/s": round(c_tf, 2),
+            "frac_of_bf16_peak": round(c_tf / PEAK_BF16_TFLOPS, 4)}
+        del cq, ckc, cvc, co, clse
+
+        # KV append of that chunk size: 8 sequences x 1024 new tokens into a cache
+        # with room for 16384 tokens each.
+        log("[bench] extra: kv append")
+        a = inputs.make_append(B, Nq, Hkv, d, 16384, seed=4321)
+        akn, avn = to_dev(a.k_new), to_dev(a.v_new)
+        akc, avc = to_dev(a.k_cache), to_dev(a.v_cache)
+        apt = torch.from_numpy(a.page_table).to(dev)
+        asp = torch.from_numpy(a.start_pos).to(dev)
+        a_ms = timed(lambda: _lib.fa_kv_append(akn, avn, akc, avc, apt, asp, stream=stream))
+        a_bytes = 2 * 2 * a.k_new.nbytes  # K and V, each read once and written once
+        a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
+        out["legs"]["kv_append"] = {
+            "num_seqs": B, "n_new": Nq, "Hkv": Hkv, "d": d, "bytes": a_bytes,
+            "ms_mean": round(a_ms, 4), "GB/s": round(a_gbs, 1),
+            "frac_of_hbm_peak": round(a_gbs / PEAK_HBM_GBS, 4)}
+        del akn, avn, akc, avc
 
     if args.calibrate_copy:
         n = 1 << 30

@@ -157,9 +157,39 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int col = lane & 31;      // query column of S^T / O^T owned by this lane
     const int g = lane >> 5;        // which half of the k-slots this lane supplies
 
-    int pair, qt;
-    map_work(blockIdx.x, n_qt, BH, H / Hkv, CAUSAL, pair, qt);
-    const int b = pair / H, h = pair % H;
+    int pair, qt, b, h;
+    if constexpr (PAGED) {
+        // Sequences of a chunked-prefill batch differ in length, so their work-groups
+        // do too. Work-groups are taken sequence by sequence, longest sequence first
+        // (ranked here from seq_lens for batches of up to 64 sequences; larger batches
+        // keep their order), so the short ones fill in behind the long ones.
+        const int per = H * n_qt, B = BH / H;
+        const int r = blockIdx.x / per;
+        map_work(blockIdx.x - r * per, n_qt, H, H / Hkv, CAUSAL, h, qt);
+        b = r;
+        if (B <= 64) {
+            __shared__ int lens_s[64];
+            __shared__ int pick_s;
+            if (tid < B) lens_s[tid] = pg.seq_lens[tid];
+            __syncthreads();
+            if (tid < B) {
+                const int mine = lens_s[tid];
+                int rank = 0;
+                for (int o = 0; o < B; ++o) {
+                    const int other = lens_s[o];
+                    rank += (other > mine) | ((other == mine) & (o < tid));
+                }
+                if (rank == r) pick_s = tid;
+            }
+            __syncthreads();
+            b = __builtin_amdgcn_readfirstlane(pick_s);
+        }
+        pair = b * H + h;
+    } else {
+        map_work(blockIdx.x, n_qt, BH, H / Hkv, CAUSAL, pair, qt);
+        b = pair / H;
+        h = pair % H;
+    }
     const int kvh = h / (H / Hkv);
     const int q0 = qt * T::BM;
     int Nk = Nk_arg;
@@ -210,12 +240,17 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             pv_off[i] = (uint32_t)(((r - 16 * w) * slot_stride) * 2 + ((pc ^ v_swz<D>(r)) * 16));
         }
     }
-    // Page id of this wave's page in tile j (-1 past the sequence).
+    // Page id of this wave's page in tile j (-1 past the sequence). The table is read
+    // through the constant address space so the uniform load is a scalar one: a vector
+    // load here would make its consumer wait for every tile load issued before it.
+    typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+    const const_i32_ptr table_row =
+        (const_i32_ptr)(pg.page_table + (PAGED ? (size_t)b * pg.max_pages : 0));
     auto page_of = [&](int j) -> int {
         if constexpr (PAGED) {
             const int pidx = 4 * j + w;
             if (pidx * 16 >= Nk) return -1;
-            return __builtin_amdgcn_readfirstlane(pg.page_table[(size_t)b * pg.max_pages + pidx]);
+            return table_row[pidx];
         }
         return -1;
     };

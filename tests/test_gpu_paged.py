@@ -76,6 +76,7 @@ def _describe(ci, what):
     (3, 8, 1, 128, 77, 77, 700, False),      # non-causal, MQA
     (2, 32, 8, 128, 1, 1, 2000, True),       # one query (decode through the prefill path)
     (5, 4, 2, 128, 17, 17, 33, True),        # lengths around page / tile boundaries
+    (70, 4, 2, 64, 16, 16, 200, True),       # more than 64 sequences (kept in order)
 ], ids=lambda x: str(x))
 def test_paged_prefill_vs_oracle(B, H, Hkv, d, Nq, lo, hi, causal):
     ci = inputs.custom_chunked_prefill(B, H, Hkv, d, Nq, lo, hi, seed=B * 31 + Nq + d)
@@ -94,6 +95,17 @@ def test_paged_prefill_page_and_tile_boundaries():
     o_h, lse_h = run_paged(ci)
     O, L = oracle_paged(ci)
     check_bf16(inputs.bf16_bits_to_f64(o_h), lse_h, O, L, "paged prefill boundaries")
+
+
+def test_paged_prefill_equal_lengths():
+    """Sequences are taken longest first; equal lengths must still each be covered once."""
+    lens = [300, 100, 300, 50, 100, 300]
+    ci = inputs.custom_chunked_prefill(len(lens), 8, 4, 128, 50, 50, 300, seq_lens=lens,
+                                       seed=13)
+    _describe(ci, "equal lengths")
+    o_h, lse_h = run_paged(ci)
+    O, L = oracle_paged(ci)
+    check_bf16(inputs.bf16_bits_to_f64(o_h), lse_h, O, L, "paged prefill equal lengths")
 
 
 @pytest.mark.parametrize("d,causal", [(128, True), (64, True), (128, False)])
