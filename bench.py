@@ -311,6 +311,25 @@ def main(argv=None):
             "frac_of_bf16_peak": round(c_tf / PEAK_BF16_TFLOPS, 4)}
         del cq, ckc, cvc, co, clse
 
+        # Sliding-window prefill: B1 H32 Hkv8 N32768 d128, causal window of 4096 keys.
+        log("[bench] extra: sliding-window prefill")
+        wB, wH, wHkv, wN, wd, wl = 1, 32, 8, 32768, 128, 4096
+        gen = torch.Generator(device=dev).manual_seed(777)
+        wq = torch.randn((wB, wH, wN, wd), generator=gen, device=dev).to(torch.bfloat16)
+        wk = torch.randn((wB, wHkv, wN, wd), generator=gen, device=dev).to(torch.bfloat16)
+        wv = torch.randn((wB, wHkv, wN, wd), generator=gen, device=dev).to(torch.bfloat16)
+        wo = torch.empty_like(wq)
+        wlse = torch.empty((wB, wH, wN), dtype=torch.float32, device=dev)
+        w_ms = timed(lambda: _lib.fa_fwd_window(wq, wk, wv, wo, wlse, window_left=wl,
+                                                window_right=0, scale=wd ** -0.5, stream=stream))
+        w_flops = 4.0 * wd * wB * wH * inputs.window_pairs(wN, wN, wl, 0)
+        w_tf = w_flops / (w_ms * 1e-3) / 1e12
+        out["legs"]["prefill_sliding_window"] = {
+            "B": wB, "H": wH, "Hkv": wHkv, "N": wN, "d": wd, "window": [wl, 0],
+            "flops": w_flops, "ms_mean": round(w_ms, 4), "TFLOP/s": round(w_tf, 2),
+            "frac_of_bf16_peak": round(w_tf / PEAK_BF16_TFLOPS, 4)}
+        del wq, wk, wv, wo, wlse
+
         # KV append of that chunk size: 8 sequences x 1024 new tokens into a cache
         # with room for 16384 tokens each.
         log("[bench] extra: kv append")

@@ -64,6 +64,22 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            void* stream);
 
 /*
+ * fa_fwd_window — fa_fwd with a sliding-window mask (glossary entry "Kayan Pencere
+ * Dikkati (Sliding Window Attention)", yapayzekasozluk.tr/etiket/attention: each token
+ * attends only the tokens within a fixed distance of its own position, so the work is
+ * O(N w) instead of O(N^2)). Query i sits at position p = Nk - Nq + i (bottom-right, as
+ * for causal) and attends keys j with p - window_left <= j <= p + window_right; -1 makes
+ * a side unbounded. The symmetric window of width w is (w/2, w/2); a causal sliding
+ * window is (w_left, 0); (-1, 0) is plain causal and (-1, -1) no mask at all.
+ * Same layouts, numerics and errors as fa_fwd; additionally Nq <= Nk and
+ * window_left, window_right >= -1 (else FA_ERR_INVALID). Every query attends at least
+ * its own position, so no row is empty.
+ */
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Hkv, int Nq, int Nk, int d, int window_left,
+                  int window_right, float scale, void* stream);
+
+/*
  * fa_fwd_fp32 — the same operation with fp32 inputs and outputs and fp32 arithmetic
  * throughout (no reduced-precision step). Same layouts, ranges and errors as fa_fwd.
  */

@@ -46,6 +46,21 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                  int H, int Hkv, int Nq, int Nk, int d, int window_left, int window_right,
+                  float scale, void* stream) {
+    // The window is placed at each query's position Nk - Nq + i, so Nq <= Nk as for causal.
+    int st = check_prefill(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, 1, scale, 2);
+    if (st != FA_OK) return st;
+    if (window_left < -1 || window_right < -1) return FA_ERR_INVALID;
+    const unsigned long long n_wg = (unsigned long long)((Nq + 127) / 128) * B * H;
+    if (n_wg >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+    hipError_t e = kvfa::launch_fwd_bf16_window(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d,
+                                                window_left, window_right, scale,
+                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
                 int H, int Hkv, int Nq, int Nk, int d, int causal, float scale, void* stream) {
     int st = check_prefill(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale, 4);

@@ -118,6 +118,19 @@ def unmasked_pairs(Nq: int, Nk: int, causal: bool) -> int:
     return Nq * (off + 1) + Nq * (Nq - 1) // 2
 
 
+def window_pairs(Nq: int, Nk: int, left: int, right: int) -> int:
+    """(query, key) pairs inside a sliding window, per (batch, head): query i at
+    position p = Nk - Nq + i counts keys max(0, p - left) .. min(Nk - 1, p + right);
+    -1 leaves a side unbounded."""
+    total = 0
+    for i in range(Nq):
+        p = Nk - Nq + i
+        lo = 0 if left < 0 else max(0, p - left)
+        hi = Nk - 1 if right < 0 else min(Nk - 1, p + right)
+        total += max(0, hi - lo + 1)
+    return total
+
+
 PREFILL_CONFIGS = {
     "fp32_single": PrefillConfig("fp32_single", 1, 1, 1, 128, 128, 64, False, "f32",
                                  1.0, 1.0 / math.sqrt(64), 1),

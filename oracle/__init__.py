@@ -18,4 +18,5 @@ from .attention import (  # noqa: F401
     online_softmax_stats,
     scatter_pages,
     softmax_rows,
+    window_mask,
 )

@@ -53,13 +53,32 @@ def _as_f64(x) -> np.ndarray:
     return a
 
 
-def allowed_keys(Nq: int, Nk: int, causal: bool) -> np.ndarray:
-    """Boolean [Nq, Nk] mask of the keys each query attends (bottom-right causal)."""
-    i = np.arange(Nq)[:, None]
+def window_mask(idx, Nq: int, Nk: int, causal: bool, window=None) -> np.ndarray:
+    """Boolean [len(idx), Nk] mask of the keys that query rows ``idx`` attend.
+
+    Query i sits at position p = i + (Nk - Nq) (bottom-right). Causal: keys j <= p.
+    Sliding window (glossary entry "Kayan Pencere Dikkati (Sliding Window
+    Attention)": a token attends only the tokens within a fixed distance of its own
+    position): ``window = (left, right)`` keeps keys p - left <= j <= p + right, where
+    -1 leaves that side unbounded; the symmetric window of width w is (w/2, w/2).
+    """
+    p = np.asarray(idx, dtype=np.int64)[:, None] + (Nk - Nq)
     j = np.arange(Nk)[None, :]
-    if not causal:
-        return np.ones((Nq, Nk), dtype=bool)
-    return j <= i + (Nk - Nq)
+    mask = np.ones((p.shape[0], Nk), dtype=bool)
+    if causal:
+        mask &= j <= p
+    if window is not None:
+        left, right = window
+        if left >= 0:
+            mask &= j >= p - left
+        if right >= 0:
+            mask &= j <= p + right
+    return mask
+
+
+def allowed_keys(Nq: int, Nk: int, causal: bool, window=None) -> np.ndarray:
+    """Boolean [Nq, Nk] mask of the keys each query attends (see ``window_mask``)."""
+    return window_mask(np.arange(Nq), Nq, Nk, causal, window)
 
 
 def softmax_rows(scores: np.ndarray, mask: np.ndarray):
@@ -79,10 +98,12 @@ def softmax_rows(scores: np.ndarray, mask: np.ndarray):
     return P, m, l
 
 
-def attention(q, k, v, *, causal: bool, scale: float, rows=None, return_probs=False):
+def attention(q, k, v, *, causal: bool, scale: float, rows=None, return_probs=False,
+              window=None):
     """Exact attention in float64.
 
     q: [B, H, Nq, d]; k, v: [B, Hkv, Nk, d] (float64, the stored values widened).
+    window: None, or (left, right) for a sliding window (``window_mask``).
     rows: None for every row, else a dict {(b, h): int array of query rows}.
     Returns (O, LSE) as dicts keyed by (b, h) when ``rows`` is given, else dense
     arrays O [B, H, Nq, d] and LSE [B, H, Nq]. With ``return_probs`` the probability
@@ -104,8 +125,7 @@ def attention(q, k, v, *, causal: bool, scale: float, rows=None, return_probs=Fa
         kvh = h // g
         # full score rows: (len(idx) x Nk), the "compatibility matrix" restricted to idx
         S = scale * (q[b, h, idx, :] @ k[b, kvh].T)
-        mask = np.ones(S.shape, dtype=bool) if not causal else \
-            (np.arange(Nk)[None, :] <= idx[:, None] + (Nk - Nq))
+        mask = window_mask(idx, Nq, Nk, causal, window)
         P, m, l = softmax_rows(S, mask)
         O = P @ v[b, kvh]
         with np.errstate(divide="ignore"):

@@ -7,15 +7,19 @@ NumPy oracle by brute force. Triple loops over Python floats, ``math.exp`` and
 Definition followed: page "Donanıma Duyarlı Algoritma Tasarımı: FlashAttention",
 section "Transformer Mimarisi ve Self-Attention Mekanizması" (softmax of the scaled
 Q K^T rows, then the weighted sum of V rows). Causal rows attend keys j <= i +
-(Nk - Nq); query head h uses key/value head h // (H // Hkv).
+(Nk - Nq); a sliding window (glossary entry "Kayan Pencere Dikkati") keeps the keys
+within (left, right) of the query's position; query head h uses key/value head
+h // (H // Hkv).
 """
 from __future__ import annotations
 
 import math
 
 
-def attention_brute(q, k, v, causal, scale):
-    """q: nested lists [B][H][Nq][d]; k, v: [B][Hkv][Nk][d]. Returns (O, LSE) lists."""
+def attention_brute(q, k, v, causal, scale, window=None):
+    """q: nested lists [B][H][Nq][d]; k, v: [B][Hkv][Nk][d]. Returns (O, LSE) lists.
+    window: None or (left, right); query i at position p = i + Nk - Nq sees keys
+    p - left .. p + right (-1: that side unbounded)."""
     B, H = len(q), len(q[0])
     Nq, d = len(q[0][0]), len(q[0][0][0])
     Hkv, Nk = len(k[0]), len(k[0][0])
@@ -26,7 +30,12 @@ def attention_brute(q, k, v, causal, scale):
         for h in range(H):
             kh = h // g
             for i in range(Nq):
-                keys = [j for j in range(Nk) if (not causal) or j <= i + (Nk - Nq)]
+                p = i + (Nk - Nq)
+                keys = [j for j in range(Nk) if (not causal) or j <= p]
+                if window is not None:
+                    lo = p - window[0] if window[0] >= 0 else -math.inf
+                    hi = p + window[1] if window[1] >= 0 else math.inf
+                    keys = [j for j in keys if lo <= j <= hi]
                 if not keys:
                     LSE[b][h][i] = -math.inf
                     continue

@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert set(declared_functions()) == {
         "fa_fwd", "fa_fwd_fp32", "fa_decode_paged", "fa_decode_paged_workspace_size",
-        "fa_decode_paged_split_tokens", "fa_fwd_paged", "fa_kv_append", "fa_status_string"}
+        "fa_decode_paged_split_tokens", "fa_fwd_paged", "fa_kv_append", "fa_fwd_window", "fa_status_string"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -69,6 +69,19 @@ def _fwd(lib, fn="fa_fwd", q=P, k=P, v=P, o=P, lse=None, B=1, H=8, Hkv=8, Nq=64,
 ])
 def test_prefill_validation(lib, fn, kw, want):
     assert _fwd(lib, fn, **kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(k=P + 8), INVALID), (dict(Nq=65, Nk=64), INVALID),
+    (dict(wl=-2), INVALID), (dict(wr=-5), INVALID), (dict(H=8, Hkv=3), INVALID),
+    (dict(scale=0.0), INVALID), (dict(d=96), UNSUPPORTED),
+])
+def test_window_validation(lib, kw, want):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, H=8, Hkv=8, Nq=64, Nk=64, d=128, wl=16, wr=0,
+             scale=0.125)
+    a.update(kw)
+    assert lib.fa_fwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"],
+                             a["Nq"], a["Nk"], a["d"], a["wl"], a["wr"], a["scale"], None) == want
 
 
 def _dec(lib, q=P, kc=P, vc=P, pt=P, sl=P, page_size=16, o=P, lse=None, S=4, H=32, Hkv=8,

@@ -101,3 +101,17 @@ def test_paged_decode_config_lengths():
     rng = np.random.default_rng(cfg.seed)
     lens = rng.integers(cfg.len_lo, cfg.len_hi, size=cfg.num_seqs, endpoint=True)
     assert lens.min() >= 512 and lens.max() <= 8192
+
+
+def test_window_pairs_matches_the_mask():
+    for Nq, Nk, left, right in ((7, 7, 2, 1), (5, 9, 0, 0), (6, 6, -1, 0), (4, 10, 3, -1),
+                                (8, 8, -1, -1), (3, 3, 100, 100)):
+        i = np.arange(Nq)[:, None] + (Nk - Nq)
+        j = np.arange(Nk)[None, :]
+        m = np.ones((Nq, Nk), bool)
+        if left >= 0:
+            m &= j >= i - left
+        if right >= 0:
+            m &= j <= i + right
+        assert inputs.window_pairs(Nq, Nk, left, right) == int(m.sum())
+    assert inputs.window_pairs(6, 6, -1, 0) == inputs.unmasked_pairs(6, 6, True)

@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 
 import oracle
+from oracle.brute import attention_brute
 from kv_cache_fa_amd import inputs
 from pins import ALL_PINS, load_golden, parse_arr, parse_num
 
@@ -175,6 +176,80 @@ def test_gather_pages_detects_a_wrong_slot():
     t = np.arange(L)
     wrong = inp.k_cache[inp.page_table[s, t // 16], (t + 1) % 16]
     assert not np.array_equal(wrong, inp.k_seq[s])
+
+
+# ---- sliding window (glossary entry "Kayan Pencere Dikkati") -----------------------
+def _rand_qkv(rng, B, H, Hkv, Nq, Nk, d):
+    return (rng.standard_normal((B, H, Nq, d)), rng.standard_normal((B, Hkv, Nk, d)),
+            rng.standard_normal((B, Hkv, Nk, d)))
+
+
+def test_window_zero_attends_only_itself():
+    """Window (0, 0): each query sees only its own position p = Nk - Nq + i, so
+    O = V[p] exactly and LSE = scale * q . k_p."""
+    rng = np.random.default_rng(0)
+    q, k, v = _rand_qkv(rng, 2, 4, 2, 5, 9, 8)
+    O, L = oracle.attention(q, k, v, causal=False, scale=0.3, window=(0, 0))
+    for b in range(2):
+        for h in range(4):
+            for i in range(5):
+                p = 9 - 5 + i
+                np.testing.assert_array_equal(O[b, h, i], v[b, h // 2, p])
+                np.testing.assert_allclose(L[b, h, i], 0.3 * q[b, h, i] @ k[b, h // 2, p],
+                                           rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("window", [(2, 1), (0, 3), (3, 0), (1, -1), (-1, 2), (4, 4)])
+def test_window_brute_force(window):
+    rng = np.random.default_rng(sum(window) + 10)
+    q, k, v = _rand_qkv(rng, 1, 2, 1, 5, 7, 4)
+    O, L = oracle.attention(q, k, v, causal=False, scale=0.5, window=window)
+    Ob, Lb = attention_brute(q.tolist(), k.tolist(), v.tolist(), False, 0.5, window=window)
+    np.testing.assert_allclose(O, np.array(Ob), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(L, np.array(Lb), rtol=0, atol=1e-13)
+
+
+def test_window_row_equals_attention_over_its_slice():
+    """A windowed row is plain (unmasked) attention over keys p-left .. p+right."""
+    rng = np.random.default_rng(4)
+    q, k, v = _rand_qkv(rng, 1, 1, 1, 12, 20, 8)
+    left, right = 5, 2
+    O, L = oracle.attention(q, k, v, causal=False, scale=0.4, window=(left, right))
+    for i in range(12):
+        p = 20 - 12 + i
+        lo, hi = max(0, p - left), min(20, p + right + 1)
+        Os, Ls = oracle.attention(q[:, :, i:i + 1], k[:, :, lo:hi], v[:, :, lo:hi],
+                                  causal=False, scale=0.4)
+        np.testing.assert_allclose(O[0, 0, i], Os[0, 0, 0], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(L[0, 0, i], Ls[0, 0, 0], rtol=0, atol=1e-14)
+
+
+def test_window_limits_are_causal_and_full():
+    """(-1, 0) is bottom-right causal and (-1, -1) is no mask."""
+    rng = np.random.default_rng(5)
+    q, k, v = _rand_qkv(rng, 1, 2, 2, 6, 10, 4)
+    for window, causal in (((-1, 0), True), ((-1, -1), False)):
+        Ow, Lw = oracle.attention(q, k, v, causal=False, scale=0.7, window=window)
+        Ob, Lb = attention_brute(q.tolist(), k.tolist(), v.tolist(), causal, 0.7)
+        np.testing.assert_allclose(Ow, np.array(Ob), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(Lw, np.array(Lb), rtol=0, atol=1e-13)
+
+
+def test_window_pins_catch_an_off_by_one_edge():
+    """A window mask with either edge moved by one key fails the slice pin."""
+    rng = np.random.default_rng(6)
+    q, k, v = _rand_qkv(rng, 1, 1, 1, 8, 12, 4)
+    left, right = 3, 1
+    for dl, dr in ((1, 0), (-1, 0), (0, 1), (0, -1)):
+        O, _ = oracle.attention(q, k, v, causal=False, scale=0.4, window=(left + dl, right + dr))
+        bad = False
+        for i in range(8):
+            p = 12 - 8 + i
+            lo, hi = max(0, p - left), min(12, p + right + 1)
+            Os, _ = oracle.attention(q[:, :, i:i + 1], k[:, :, lo:hi], v[:, :, lo:hi],
+                                     causal=False, scale=0.4)
+            bad |= not np.allclose(O[0, 0, i], Os[0, 0, 0], rtol=0, atol=1e-12)
+        assert bad, (dl, dr)
 
 
 def test_scatter_pages_hand_worked():
