@@ -36,7 +36,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
-    "fwd_bf16_kernel": os.path.join(ROOT, "kv_cache_fa_amd", "csrc", "prefill_bf16.hip"),
+    "fwd_pp_kernel": os.path.join(ROOT, "kv_cache_fa_amd", "csrc", "prefill_pp.hip"),
     "decode_split_kernel": os.path.join(ROOT, "kv_cache_fa_amd", "csrc", "decode.hip"),
 }
 
@@ -200,7 +200,7 @@ def main(argv=None):
     p_tflops = p_flops / (p_ms.mean() * 1e-3) / 1e12
     d_gbs = d_bytes / (d_ms.mean() * 1e-3) / 1e9
 
-    p_traffic = measured_traffic("fwd_bf16_kernel", pcfg.name)
+    p_traffic = measured_traffic("fwd_pp_kernel", pcfg.name)
     d_traffic = measured_traffic("decode_split_kernel", dcfg.name)
     out = {
         "metric": METRIC,
@@ -226,7 +226,7 @@ def main(argv=None):
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "fwd_bf16_kernel",
+            "kernel": "fwd_pp_kernel",
             "bound": "mfma",
             "achieved": round(p_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,

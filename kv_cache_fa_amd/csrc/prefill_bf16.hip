@@ -1,4 +1,7 @@
-// bf16 exact attention (prefill) on gfx950 MFMA, fp32 accumulation.
+// bf16 exact attention (prefill) on gfx950 MFMA, fp32 accumulation: the four-wave kernel
+// behind chunked prefill through the page table (fa_fwd_paged) and sliding-window
+// prefill (fa_fwd_window). Contiguous full / causal prefill (fa_fwd) runs the ping-pong
+// kernel of prefill_pp.hip, which does the same arithmetic in the same order.
 //
 // Method (page "Donanıma Duyarlı Algoritma Tasarımı: FlashAttention"):
 // * K and V are split into tiles that are staged in LDS, the CU's fast on-chip
@@ -17,16 +20,16 @@
 //
 // gfx950 mapping (this design, not the pages'):
 // * 256 threads = 4 waves; each wave owns 32 query rows (BM = 128 rows per
-//   work-group). BN = 64 keys per tile for d = 128, 128 keys for d = 64, so a K
-//   tile is always 16 KiB; K and V^T tiles are double-buffered (64 KiB of LDS, two
-//   work-groups per CU).
+//   work-group); 64 keys per tile. K and V tiles go from HBM straight into LDS
+//   (buffer_load ... lds) with XOR-swizzled 16-byte chunks, double-buffered (64 KiB of
+//   LDS, two work-groups per CU).
 // * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //   A = K rows read from LDS, B = the wave's Q held in registers. Each lane then
 //   owns one query column, so the row max and row sum are in-lane reductions plus
 //   a single exchange with lane ^ 32.
 // * The output is also accumulated transposed, O^T += V^T P^T: B = P^T comes
-//   straight from the score registers (converted to bf16), A = V^T read from a
-//   transposed LDS copy of the V tile. The key order inside each 16-key MFMA step
+//   straight from the score registers (converted to bf16), A = V^T read from the V
+//   tile through transposing LDS reads. The key order inside each 16-key MFMA step
 //   follows the score accumulator layout; any order is valid for a sum over keys as
 //   long as A and B agree.
 // * Softmax uses exp2 with scale*log2(e) folded into one FMA per score. The
@@ -42,10 +45,12 @@
 
 #include "common.h"
 #include "launch.h"
+#include "prefill_common.h"
 
 namespace kvfa {
 
 namespace {
+using namespace prefill;
 
 template <int D>
 struct Tile {
@@ -63,58 +68,6 @@ struct Tile {
     static_assert(DMA >= 1 && DMA * 1024 * (NT / 64) == TILE, "whole 1 KiB loads per wave");
 };
 
-// XOR swizzles of the 16-byte chunks of a tile row (a direct-to-LDS load writes 1 KiB
-// contiguously, so rows cannot be padded). K: the 16 rows read together by a 16-lane
-// group for one MFMA operand land on 16 different bank groups. V: the 4 rows gathered by
-// one transposing read land on 4 different 64-byte bank groups.
-template <int D>
-__device__ __forceinline__ int k_swz(int row) {
-    if constexpr (D == 128) return row & 15;
-    else return (row >> 1) & 7;
-}
-template <int D>
-__device__ __forceinline__ int v_swz(int row) {
-    if constexpr (D == 128) return 4 * (row & 3);
-    else return 4 * ((row >> 1) & 1);
-}
-
-// Work-group id -> (batch*H + head, q tile). The dispatcher places work-group i on XCD
-// i % 8, and each XCD has its own L2. When the (batch, head) count is a multiple of 8,
-// XCD x owns a contiguous block of (batch, head) pairs; if that block holds whole GQA
-// groups (the g query heads that read one K/V head), the XCD finishes one group's q
-// tiles before starting the next, so its L2 only has to hold one K/V head at a time.
-// Within that order causal q tiles run longest first.
-__device__ __forceinline__ void map_work(int id, int n_qt, int BH, int g, bool causal,
-                                         int& pair, int& qt) {
-    int r;
-    if ((BH & 7) == 0) {
-        const int per = BH >> 3, slot = id >> 3, x = id & 7;
-        if (per % g == 0) {
-            const int span = g * n_qt;              // work-groups of one GQA group
-            const int grp = slot / span, rem = slot % span;
-            pair = x * per + grp * g + rem % g;
-            r = rem / g;
-        } else {
-            pair = x * per + slot % per;
-            r = slot / per;
-        }
-    } else {
-        pair = id % BH;
-        r = id / BH;
-    }
-    qt = causal ? n_qt - 1 - r : r;
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// Transposing LDS read (ds_read_b64_tr_b16). Within each 16-lane group, source lane
-// a + 4e points at 4 consecutive bf16 of row e (e = 0..3), column block a; lane i of
-// the group receives column i of rows 0..3.
-__device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
-    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) char*)p);
-    return __builtin_bit_cast(u32x2, v);
-}
 
 // Per-iteration schedule of one wave (tile j):
 //   issue S_{j+1} = K_{j+1} Q^T on MFMA  |  softmax of S_j on the VALU (mask, running max,
@@ -539,13 +492,6 @@ hipError_t launch_dispatch(const void* q, const void* k, const void* v, void* o,
 }
 
 }  // namespace
-
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-                           hipStream_t stream) {
-    return launch_dispatch<false>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale,
-                                  PagedKV{nullptr, nullptr, 0, 0, 0}, stream);
-}
 
 hipError_t launch_fwd_bf16_window(const void* q, const void* k, const void* v, void* o,
                                   float* lse, int B, int H, int Hkv, int Nq, int Nk, int d,

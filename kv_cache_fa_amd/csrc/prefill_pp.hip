@@ -1,0 +1,342 @@
+// bf16 exact attention (prefill, contiguous K/V) on gfx950: the ping-pong kernel.
+//
+// Method (page "Donanıma Duyarlı Algoritma Tasarımı: FlashAttention"): Q, K and V are
+// processed in tiles held on chip ("FlashAttention'ın Temelleri"); every query row keeps
+// a running max and sum merged tile by tile ("Online Softmax Prensibi", steps 1-5) and
+// the output accumulator is rescaled by the same factor, so one pass over K/V suffices;
+// work is split over query rows and the next K/V tiles are fetched while the current
+// ones are used ("FlashAttention-2: Optimizasyonlar ve İyileştirmeler", items 1-2). GQA:
+// query head h reads K/V head h / (H / Hkv) (glossary entry "KV Cache (Anahtar-Değer
+// Önbelleği)", yapayzekasozluk.tr/etiket/attention).
+//
+// gfx950 mapping (this design, not the pages'):
+// * A SIMD issues a wave's MFMAs and its ordinary VALU work one after the other, but
+//   overlaps the MFMAs of one wave with the VALU work of another. So each work-group has
+//   8 waves, two per SIMD, in two groups: A = waves 0-3 (query rows 0-127 of a 256-row
+//   tile), B = waves 4-7 (rows 128-255). Time is cut into slots separated by work-group
+//   barriers; in every slot one group runs its matrix phase (S_j = K_j Q^T and
+//   O^T += V_{j-1}^T P_{j-1}^T, 32 MFMAs per wave) while the other runs its softmax
+//   phase (mask, running max, exponentials of S into P), and the groups swap each slot.
+// * Per wave: 32 query rows, one per lane column, so the row max and sum are in-lane
+//   reductions plus one v_permlane32_swap; scores are computed transposed
+//   (v_mfma_f32_32x32x16_bf16 with K rows from LDS as A and the wave's Q in registers as
+//   B) and so is the output (V^T from LDS through transposing reads as A, P^T from the
+//   score registers as B).
+// * K and V tiles of 64 keys go from HBM straight into LDS (buffer_load ... lds) with
+//   XOR-swizzled 16-byte chunks (conflict-free operand reads), double-buffered: tile j+1
+//   of K and tile j of V are loaded during period j (two slots) and published by the
+//   barrier that ends it. 64 KiB of LDS, one work-group per CU.
+// * The reference max used for the exponentials only moves when the row max grows by
+//   more than 8 (log2 units); exponentials stay below 2^8 and the result is unchanged
+//   because softmax(x) = softmax(x - c) ("FlashAttention'ın Temelleri").
+// * Causal: the work-group visits the key tiles its last row needs; a wave skips the
+//   tiles entirely in its rows' future, and only tiles crossing a wave's diagonal (or
+//   Nk) are masked.
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+#include "prefill_common.h"
+
+namespace kvfa {
+
+namespace {
+using namespace prefill;
+
+template <int D>
+struct TilePP {
+    static constexpr int NW = 8;                // waves per work-group
+    static constexpr int NT = 64 * NW;
+    static constexpr int BM = 32 * NW;          // query rows per work-group
+    static constexpr int BN = 64;               // keys per tile
+    static constexpr int KB = BN / 32;          // 32-key blocks of S^T
+    static constexpr int KS = D / 16;           // MFMA k-steps of Q.K
+    static constexpr int DB = D / 32;           // 32-dim blocks of O^T
+    static constexpr int PS = BN / 16;          // MFMA k-steps of P.V
+    static constexpr int ROW = D * 2;           // bytes per K/V row
+    static constexpr int TILE = BN * ROW;       // bytes of one K (or V) tile
+    static constexpr int DMA = TILE / 1024 / NW;  // 1 KiB direct loads per wave per tile
+    static_assert(DMA >= 1 && DMA * 1024 * NW == TILE, "whole 1 KiB loads per wave");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                   const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
+                   float* __restrict__ lse, int H, int Hkv, int Nq, int Nk, int n_qt, int BH,
+                   float scale_log2, float tau_raw) {
+    using T = TilePP<D>;
+    constexpr int BN = T::BN;
+    __shared__ __attribute__((aligned(1024))) char ks0[T::TILE];
+    __shared__ __attribute__((aligned(1024))) char ks1[T::TILE];
+    __shared__ __attribute__((aligned(1024))) char vs0[T::TILE];
+    __shared__ __attribute__((aligned(1024))) char vs1[T::TILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+    const int grp = w >> 2;                                    // 0: group A, 1: group B
+    const int col = lane & 31;  // query column of S^T / O^T owned by this lane
+    const int g = lane >> 5;    // which half of the k-slots this lane supplies
+
+    int pair, qt;
+    map_work(blockIdx.x, n_qt, BH, H / Hkv, CAUSAL, pair, qt);
+    const int b = pair / H, h = pair % H;
+    const int kvh = h / (H / Hkv);
+    const int q0 = qt * T::BM;
+    const int off = Nk - Nq;
+    const int wrow0 = q0 + w * 32;  // first query row of this wave
+    const int qrow = wrow0 + col;
+
+    const auto rq = make_rsrc(q + (size_t)pair * Nq * D, (uint32_t)Nq * D * 2);
+    const auto rk = make_rsrc(k + ((size_t)b * Hkv + kvh) * Nk * D, (uint32_t)Nk * D * 2);
+    const auto rv = make_rsrc(v + ((size_t)b * Hkv + kvh) * Nk * D, (uint32_t)Nk * D * 2);
+
+    // B operand of S^T = K Q^T: Q[qrow][16s + 8g .. +7]; rows past Nq load as zero.
+    u32x4 qf[T::KS];
+#pragma unroll
+    for (int s = 0; s < T::KS; ++s)
+        qf[s] = buf_load16(rq, (uint32_t)(qrow * D + s * 16 + g * 8) * 2);
+
+    // Tiles of the work-group (every wave steps through them for the barriers), tiles
+    // this wave computes (n_w), and the first one it must mask (full_w).
+    const int n_all = (Nk + BN - 1) / BN;
+    int n_tiles = n_all, n_w = n_all, full_w = Nk / BN;
+    if (CAUSAL) {
+        const int last_row = min(q0 + T::BM, Nq) - 1;
+        n_tiles = min(n_all, (last_row + off) / BN + 1);
+        const int wlast = min(wrow0 + 31, Nq - 1);
+        n_w = wrow0 < Nq ? min(n_all, (wlast + off) / BN + 1) : 0;
+        full_w = min(full_w, (wrow0 + off + 1) / BN);
+    } else if (wrow0 >= Nq) {
+        n_w = 0;
+    }
+
+    // Direct loads: the wave's i-th 1 KiB piece of a tile covers tile bytes
+    // [1024 (DMA w + i), +1024); lane L fills byte 16 L of it, i.e. row r, physical chunk
+    // pc, with logical chunk pc ^ swizzle(r) of row r.
+    uint32_t dk_off[T::DMA], dv_off[T::DMA];
+#pragma unroll
+    for (int i = 0; i < T::DMA; ++i) {
+        const int byte = 1024 * (T::DMA * w + i) + 16 * lane;
+        const int r = byte / T::ROW, pc = (byte % T::ROW) / 16;
+        dk_off[i] = (uint32_t)(r * T::ROW + ((pc ^ k_swz<D>(r)) * 16));
+        dv_off[i] = (uint32_t)(r * T::ROW + ((pc ^ v_swz<D>(r)) * 16));
+    }
+    auto load_k = [&](int j, char* dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < T::DMA; ++i)
+            buf_load16_lds(rk, dst + 1024 * (T::DMA * w + i), dk_off[i], (uint32_t)(j * T::TILE));
+    };
+    auto load_v = [&](int j, char* dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < T::DMA; ++i)
+            buf_load16_lds(rv, dst + 1024 * (T::DMA * w + i), dv_off[i], (uint32_t)(j * T::TILE));
+    };
+
+    // Per-lane LDS read offsets. K operand (kb, s): row 32 kb + col, logical chunk 2s + g.
+    // V^T operand (t, db, half): rows 16t + 8 half + 4(G/2) + e, logical chunk
+    // 4 db + 2(G%2) + a/2, byte 8(a%2) in it (G = lane/16, lane%16 = a + 4e).
+    int kr_off[T::KS];
+#pragma unroll
+    for (int s = 0; s < T::KS; ++s)
+        kr_off[s] = col * T::ROW + (((2 * s + g) ^ k_swz<D>(col)) * 16);
+    const int vG = lane >> 4, va = lane & 3, ve = (lane >> 2) & 3;
+    const int vrow = (vG >> 1) * 4 + ve;
+    int vr_off[T::DB];
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+        vr_off[db] = vrow * T::ROW + (((4 * db + 2 * (vG & 1) + (va >> 1)) ^ v_swz<D>(vrow)) * 16) +
+                     8 * (va & 1);
+
+    float m_used = -INFINITY;  // raw-score reference max of this lane's query
+    float l_part = 0.f;        // this lane's share of the row sum
+    f32x16 oacc[T::DB];
+#pragma unroll
+    for (int i = 0; i < T::DB; ++i) oacc[i] = f32x16{};
+    f32x16 sacc[T::KB];  // S^T of the tile between its matrix and softmax phases
+    u32x4 pf[T::PS];     // P^T (bf16) of the tile between its softmax and matrix phases
+
+    // Matrix phase: S_j = K_j Q^T (if qk) and O^T += V_{j-1}^T P_{j-1}^T (if pv).
+    auto matrix_phase = [&](const char* kst, const char* vst, bool qk, bool pv)
+                            __attribute__((always_inline)) {
+        if (qk) {
+#pragma unroll
+            for (int kb = 0; kb < T::KB; ++kb) {
+                sacc[kb] = f32x16{};
+#pragma unroll
+                for (int s = 0; s < T::KS; ++s) {
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(kst + kr_off[s] + kb * 32 * T::ROW);
+                    sacc[kb] = mfma32x32x16(a, qf[s], sacc[kb]);
+                }
+            }
+            // Each K operand read goes three MFMAs ahead of its use.
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS reads
+#pragma unroll
+            for (int i = 0; i < T::KB * T::KS - 3; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+        }
+        if (pv) {
+#pragma unroll
+            for (int t = 0; t < T::PS; ++t)
+#pragma unroll
+                for (int db = 0; db < T::DB; ++db) {
+                    // keys 16t + 4g + {0..3} and 16t + 8 + 4g + {0..3} at dim 32db + col
+                    const u32x2 a0 = lds_read_tr(vst + vr_off[db] + (t * 16) * T::ROW);
+                    const u32x2 a1 = lds_read_tr(vst + vr_off[db] + (t * 16 + 8) * T::ROW);
+                    const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
+                    oacc[db] = mfma32x32x16(a, pf[t], oacc[db]);
+                }
+            // The V^T operand reads go two MFMAs ahead of their use.
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < T::PS * T::DB - 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+    };
+
+    // Softmax phase of tile j: mask, running max (lazy reference), P = exp2 into pf.
+    auto softmax_phase = [&](const int j) __attribute__((always_inline)) {
+        if (j >= full_w) {
+            // key offset inside the tile of element (kb, i) is kb*32 + 8*(i/4) + 4g + i%4;
+            // it is dead past the row's last key and past Nk.
+            int lim = Nk - 1 - j * BN - 4 * g;
+            if (CAUSAL) lim = min(lim, qrow + off - j * BN - 4 * g);
+#pragma unroll
+            for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sacc[kb][i] = -INFINITY;
+        }
+        // Every row attends key 0, so after its first tile the max is finite.
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+        mx = fmaxf(mx, xor32(mx));
+        const float m_cand = fmaxf(m_used, mx);
+        const bool move = m_cand > m_used + tau_raw;
+        if (__builtin_amdgcn_ballot_w64(move)) {
+            // Only rows whose max moved change their reference (alpha = 1 elsewhere), so
+            // a row's arithmetic never depends on the other rows of the wave.
+            const float m_new = move ? m_cand : m_used;
+            const float alpha = move ? fast_exp2((m_used - m_new) * scale_log2) : 1.f;
+            m_used = m_new;
+            l_part *= alpha;
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        }
+        const float mb = m_used * scale_log2;
+#pragma unroll
+        for (int t = 0; t < T::PS; ++t) {
+            const int kb = t >> 1, base = (t & 1) * 8;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float p0 = fast_exp2(fmaf(sacc[kb][base + 2 * u], scale_log2, -mb));
+                const float p1 = fast_exp2(fmaf(sacc[kb][base + 2 * u + 1], scale_log2, -mb));
+                pf[t][u] = pack_bf16x2(p0, p1);
+                l_part += p0 + p1;  // fp32 sum of the unrounded exponentials
+            }
+        }
+    };
+
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    // Period j = slots 2j and 2j+1; K_j is in stage j&1, V_{j-1} in stage (j-1)&1.
+    //   slot 2j:   A: matrix phase (QK_j, PV_{j-1})   B: softmax of tile j-1
+    //   slot 2j+1: B: matrix phase (QK_j, PV_{j-1})   A: softmax of tile j
+    // K_{j+1} and V_j are loaded at the start of the period; the barrier that ends it
+    // (after each wave's own loads complete) publishes them. The barrier between the two
+    // slots waits for nothing but the other group. Each group runs its own copy of the
+    // loop (the same number of barriers), straight-line code for one role.
+    auto period = [&](const int j, auto par, auto role) __attribute__((always_inline)) {
+        constexpr int pv = decltype(par)::value;
+        constexpr bool is_a = decltype(role)::value == 0;
+        const char* k_cur = pv ? ks1 : ks0;   // K_j
+        char* k_nxt = pv ? ks0 : ks1;         // receives K_{j+1}
+        const char* v_prev = pv ? vs0 : vs1;  // V_{j-1}
+        char* v_cur = pv ? vs1 : vs0;         // receives V_j
+        if (j + 1 < n_tiles) load_k(j + 1, k_nxt);
+        if (j < n_tiles) load_v(j, v_cur);
+        const bool qk = j < n_w, pvv = j >= 1 && j - 1 < n_w;
+        if constexpr (is_a) {
+            matrix_phase(k_cur, v_prev, qk, pvv);
+            __builtin_amdgcn_s_barrier();
+            if (qk) softmax_phase(j);
+        } else {
+            if (pvv) softmax_phase(j - 1);
+            __builtin_amdgcn_s_barrier();
+            matrix_phase(k_cur, v_prev, qk, pvv);
+        }
+        __syncthreads();
+    };
+    auto run = [&](auto role) __attribute__((always_inline)) {
+        int j = 0;
+        for (; j + 1 <= n_tiles; j += 2) {
+            period(j, P0{}, role);
+            period(j + 1, P1{}, role);
+        }
+        if (j <= n_tiles) period(j, P0{}, role);  // periods 0 .. n_tiles
+    };
+
+    load_k(0, ks0);
+    __syncthreads();
+    if (grp == 0) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
+
+    // ---- epilogue: O = O_acc / l, lse = M + ln L ----
+    const float l = l_part + xor32(l_part);
+    if (qrow < Nq) {
+        const float inv = 1.f / l;
+        uint16_t* orow = o + ((size_t)pair * Nq + qrow) * D;
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d0 = db * 32 + r * 8 + g * 4;
+                u32x2 pk = {pack_bf16x2(oacc[db][r * 4 + 0] * inv, oacc[db][r * 4 + 1] * inv),
+                            pack_bf16x2(oacc[db][r * 4 + 2] * inv, oacc[db][r * 4 + 3] * inv)};
+                *reinterpret_cast<u32x2*>(orow + d0) = pk;
+            }
+        if (lse != nullptr && g == 0)
+            lse[(size_t)pair * Nq + qrow] = (m_used * scale_log2 + fast_log2(l)) * kLn2;
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_pp(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int Hkv, int Nq, int Nk, float scale, hipStream_t stream) {
+    using T = TilePP<D>;
+    const int n_qt = (Nq + T::BM - 1) / T::BM;
+    const int BH = B * H;
+    const float scale_log2 = scale * kLog2e;
+    const float tau_raw = 8.0f / scale_log2;  // move the reference max past +8 in log2 units
+    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL>), dim3(n_qt * BH), dim3(T::NT), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, H, Hkv,
+                       Nq, Nk, n_qt, BH, scale_log2, tau_raw);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                           hipStream_t stream) {
+    if (d == 128)
+        return causal ? launch_pp<128, true>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream)
+                      : launch_pp<128, false>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream);
+    return causal ? launch_pp<64, true>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream)
+                  : launch_pp<64, false>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream);
+}
+
+}  // namespace kvfa
