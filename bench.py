@@ -284,6 +284,16 @@ def main(argv=None):
             "B": gcfg.B, "H": gcfg.H, "Hkv": gcfg.Hkv, "N": gcfg.Nq, "d": gcfg.d,
             "ms_mean": round(g_ms, 4), "TFLOP/s": round(g_tf, 2),
             "frac_of_bf16_peak": round(g_tf / PEAK_BF16_TFLOPS, 4)}
+        # The same workload through the FlashAttention-1 two-pass path (statistics pass +
+        # output pass); TFLOP/s counts the algorithmic flops, not the recomputed Q.K^T.
+        log("[bench] extra: gqa_causal two-pass")
+        t_ms = timed(lambda: _lib.fa_fwd_two_pass(gq, gk, gv, go, glse, causal=True,
+                                                  scale=gcfg.scale, stream=stream))
+        t_tf = gcfg.flops / (t_ms * 1e-3) / 1e12
+        out["legs"]["prefill_gqa_causal_two_pass"] = {
+            "ms_mean": round(t_ms, 4), "TFLOP/s": round(t_tf, 2),
+            "frac_of_bf16_peak": round(t_tf / PEAK_BF16_TFLOPS, 4),
+            "mfma_flops_executed_per_algorithmic": 1.5}
         del gq, gk, gv, go, glse
 
     if not args.no_extra:

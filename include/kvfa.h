@@ -64,6 +64,23 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            void* stream);
 
 /*
+ * fa_fwd_two_pass — fa_fwd computed in the two passes of FlashAttention-1 (page
+ * "Donanıma Duyarlı Algoritma Tasarımı: FlashAttention", section "FlashAttention-1
+ * (İki Geçişli Yaklaşım)"): the first pass reads Q and K and writes only each row's
+ * softmax statistics to HBM; the second reads Q, K, V and those statistics again,
+ * recomputes the scores, normalises them with the statistics and accumulates the
+ * output. It costs one more Q.K^T than fa_fwd and serves as an independent check of the
+ * single-pass recurrence.
+ * Same layouts, ranges and errors as fa_fwd, except that lse is REQUIRED (NULL gives
+ * FA_ERR_INVALID): the statistics travel between the passes through it, as
+ * lse = M + ln L, and it holds the result's lse on return. Numerics: as fa_fwd, with P
+ * normalised before its rounding to bf16.
+ */
+int fa_fwd_two_pass(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                    void* stream);
+
+/*
  * fa_fwd_window — fa_fwd with a sliding-window mask (glossary entry "Kayan Pencere
  * Dikkati (Sliding Window Attention)", yapayzekasozluk.tr/etiket/attention: each token
  * attends only the tokens within a fixed distance of its own position, so the work is

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     fa_fwd,
     fa_fwd_fp32,
     fa_fwd_paged,
+    fa_fwd_two_pass,
     fa_fwd_window,
     fa_kv_append,
     fa_status_string,

@@ -26,6 +26,7 @@ SIGNATURES = {
     "fa_decode_paged_split_tokens": (_i, [_i, _i, _i, _i]),
     "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                              _f, _vp, _sz, _vp]),
+    "fa_fwd_two_pass": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp]),
     "fa_fwd_window": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp]),
     "fa_fwd_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                           _i, _f, _vp]),
@@ -108,6 +109,23 @@ def fa_fwd(q, k, v, o, lse=None, *, causal: bool, scale: float, stream=None):
         _require(tuple(lse.shape) == (B, H, Nq), "lse must be [B,H,Nq]")
     _check("fa_fwd", lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Nq,
                                   Nk, d, int(bool(causal)), float(scale), _stream(stream)))
+
+
+def fa_fwd_two_pass(q, k, v, o, lse, *, causal: bool, scale: float, stream=None):
+    """bf16 prefill in two passes (statistics, then output); lse [B,H,Nq] fp32 required."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check_tensor(t, torch.bfloat16, n)
+    B, H, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    _require(tuple(k.shape) == tuple(v.shape) == (B, Hkv, Nk, d), "k/v shape mismatch")
+    _require(tuple(o.shape) == tuple(q.shape), "o must have q's shape")
+    _require(lse is not None, "lse is required: it carries the statistics between the passes")
+    _check_tensor(lse, torch.float32, "lse")
+    _require(tuple(lse.shape) == (B, H, Nq), "lse must be [B,H,Nq]")
+    _check("fa_fwd_two_pass", lib().fa_fwd_two_pass(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Nq, Nk, d, int(bool(causal)),
+        float(scale), _stream(stream)))
 
 
 def fa_fwd_window(q, k, v, o, lse=None, *, window_left: int, window_right: int, scale: float,

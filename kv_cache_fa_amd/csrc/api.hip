@@ -46,6 +46,20 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_fwd_two_pass(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                    void* stream) {
+    if (!lse) return FA_ERR_INVALID;  // carries the row statistics between the passes
+    int st = check_prefill(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale, 2);
+    if (st != FA_OK) return st;
+    const unsigned long long n_wg = (unsigned long long)((Nq + 127) / 128) * B * H;
+    if (n_wg >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+    hipError_t e = kvfa::launch_fwd_bf16_two_pass(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d,
+                                                  causal != 0, scale,
+                                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                   int H, int Hkv, int Nq, int Nk, int d, int window_left, int window_right,
                   float scale, void* stream) {

@@ -17,6 +17,10 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                            hipStream_t stream);
 
+hipError_t launch_fwd_bf16_two_pass(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, int B, int H, int Hkv, int Nq, int Nk, int d,
+                                    int causal, float scale, hipStream_t stream);
+
 hipError_t launch_fwd_bf16_window(const void* q, const void* k, const void* v, void* o,
                                   float* lse, int B, int H, int Hkv, int Nq, int Nk, int d,
                                   int window_left, int window_right, float scale,

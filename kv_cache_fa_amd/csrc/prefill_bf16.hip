@@ -102,7 +102,13 @@ struct Window {
     int left, right;
 };
 
-template <int D, bool CAUSAL, bool PAGED, bool WINDOW>
+// Two passes (PASS = 1, then PASS = 2; page "Donanıma Duyarlı Algoritma Tasarımı:
+// FlashAttention", section "FlashAttention-1 (İki Geçişli Yaklaşım)"): the first pass
+// sweeps K only and keeps each row's running max and sum, leaving the row statistics in
+// HBM as lse = M + ln L; the second recomputes the scores, normalises them directly with
+// those statistics (P = exp(scale s - lse)) and accumulates P V, with no rescaling.
+// PASS = 0 is the usual single pass.
+template <int D, bool CAUSAL, bool PAGED, bool WINDOW, int PASS = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
@@ -273,6 +279,9 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         vr_off[db] = vrow * T::ROW + (((4 * db + 2 * (vG & 1) + (va >> 1)) ^ v_swz<D>(vrow)) * 16) +
                      8 * (va & 1);
 
+    // Second pass: the row's statistics in log2 units (rows past Nq are never stored).
+    float mb_fixed = 0.f;
+    if constexpr (PASS == 2) mb_fixed = qrow < Nq ? lse[(size_t)pair * Nq + qrow] * kLog2e : 0.f;
     float m_used = -INFINITY;  // raw-score reference max of this lane's query
     float l_part = 0.f;        // this lane's share of the row sum
     f32x16 oacc[T::DB];
@@ -327,6 +336,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         // so after the first tile the max is finite and no -inf - -inf can occur; with a
         // window the reference stays -inf until the row's first key and is then moved
         // (alpha = 0 clears nothing but zeros).
+        if constexpr (PASS != 2) {
         float mx = sacc[0][0];
 #pragma unroll
         for (int kb = 0; kb < T::KB; ++kb)
@@ -344,12 +354,16 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             const float alpha = move ? fast_exp2((m_used - m_new) * scale_log2) : 1.f;
             m_used = m_new;
             l_part *= alpha;
+            if constexpr (PASS == 0) {
 #pragma unroll
-            for (int db = 0; db < T::DB; ++db)
+                for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+            }
         }
-        const float mb = (WINDOW && m_used == -INFINITY) ? 0.f : m_used * scale_log2;
+        }
+        const float mb = PASS == 2 ? mb_fixed
+                                   : (WINDOW && m_used == -INFINITY) ? 0.f : m_used * scale_log2;
 #pragma unroll
         for (int t = 0; t < T::PS; ++t) {
             const int kb = t >> 1, base = (t & 1) * 8;
@@ -359,25 +373,29 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 const float p0 = fast_exp2(fmaf(sacc[kb][base + 2 * u], scale_log2, -mb));
                 const float p1 = fast_exp2(fmaf(sacc[kb][base + 2 * u + 1], scale_log2, -mb));
                 pf[u] = pack_bf16x2(p0, p1);
-                l_part += p0 + p1;  // fp32 sum of the unrounded exponentials
+                if constexpr (PASS != 2) l_part += p0 + p1;  // fp32 sum of the unrounded exponentials
             }
+            if constexpr (PASS != 1) {
 #pragma unroll
-            for (int db = 0; db < T::DB; ++db) {
-                // keys 16t + 4g + {0..3} and 16t + 8 + 4g + {0..3} at dim 32db + col
-                const u32x2 a0 = lds_read_tr(vst + vr_off[db] + (t * 16) * T::ROW);
-                const u32x2 a1 = lds_read_tr(vst + vr_off[db] + (t * 16 + 8) * T::ROW);
-                const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
-                oacc[db] = mfma32x32x16(a, pf, oacc[db]);
+                for (int db = 0; db < T::DB; ++db) {
+                    // keys 16t + 4g + {0..3} and 16t + 8 + 4g + {0..3} at dim 32db + col
+                    const u32x2 a0 = lds_read_tr(vst + vr_off[db] + (t * 16) * T::ROW);
+                    const u32x2 a1 = lds_read_tr(vst + vr_off[db] + (t * 16 + 8) * T::ROW);
+                    const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
+                    oacc[db] = mfma32x32x16(a, pf, oacc[db]);
+                }
             }
         }
-        // Schedule: the V^T operand reads go two MFMAs ahead of their use.
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        if constexpr (PASS != 1) {
+            // Schedule: the V^T operand reads go two MFMAs ahead of their use.
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-        for (int i = 0; i < T::PS * T::DB - 2; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            for (int i = 0; i < T::PS * T::DB - 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     };
 
     using P0 = std::integral_constant<int, 0>;
@@ -391,7 +409,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         char* v_cur = pv ? vs1 : vs0;   // V_j
         char* v_nxt = pv ? vs0 : vs1;   // receives V_{j+1}
         if (j + 2 < j_end) load_k(j + 2, k_cur);
-        if (j + 1 < j_end) load_v(j + 1, v_nxt);
+        if (PASS != 1 && j + 1 < j_end) load_v(j + 1, v_nxt);
         if constexpr (PAGED) {  // page ids for the next step's loads
             pid_v = pid_k;
             pid_k = page_of(j + 3);
@@ -416,7 +434,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         pid_v = pv_save;
     } else {
         load_k(j_begin, ks0);
-        load_v(j_begin, vs0);
+        if (PASS != 1) load_v(j_begin, vs0);
         if (j_begin + 1 < j_end) load_k(j_begin + 1, ks1);
     }
     __syncthreads();
@@ -446,8 +464,13 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
     // ---- epilogue: O = O_acc / l, lse = M + ln L ----
     const float l = l_part + xor32(l_part);
+    if (PASS == 1) {  // statistics only
+        if (qrow < Nq && g == 0)
+            lse[(size_t)pair * Nq + qrow] = (m_used * scale_log2 + fast_log2(l)) * kLn2;
+        return;
+    }
     if (qrow < Nq) {
-        const float inv = 1.f / l;
+        const float inv = PASS == 2 ? 1.f : 1.f / l;  // the second pass is normalised already
         uint16_t* orow = o + ((size_t)pair * Nq + qrow) * D;
 #pragma unroll
         for (int db = 0; db < T::DB; ++db)
@@ -458,12 +481,12 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                             pack_bf16x2(oacc[db][r * 4 + 2] * inv, oacc[db][r * 4 + 3] * inv)};
                 *reinterpret_cast<u32x2*>(orow + d0) = pk;
             }
-        if (lse != nullptr && g == 0)
+        if (PASS == 0 && lse != nullptr && g == 0)
             lse[(size_t)pair * Nq + qrow] = (m_used * scale_log2 + fast_log2(l)) * kLn2;
     }
 }
 
-template <int D, bool CAUSAL, bool PAGED, bool WINDOW = false>
+template <int D, bool CAUSAL, bool PAGED, bool WINDOW = false, int PASS = 0>
 hipError_t launch_typed(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                         int H, int Hkv, int Nq, int Nk, float scale, PagedKV pg,
                         hipStream_t stream, Window win = Window{0, 0}) {
@@ -472,7 +495,7 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, void* o, fl
     const int BH = B * H;
     const float scale_log2 = scale * kLog2e;
     const float tau_raw = 8.0f / scale_log2;  // move the reference max past +8 in log2 units
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PAGED, WINDOW>), dim3(n_qt * BH),
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PAGED, WINDOW, PASS>), dim3(n_qt * BH),
                        dim3(T::NT), 0, stream, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                        static_cast<uint16_t*>(o), lse, H, Hkv, Nq, Nk, n_qt, BH, scale_log2,
@@ -505,6 +528,27 @@ hipError_t launch_fwd_bf16_window(const void* q, const void* k, const void* v, v
                                                      none, stream, win);
     return launch_typed<64, false, false, true>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, none,
                                                 stream, win);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_two_pass(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                           int H, int Hkv, int Nq, int Nk, float scale, hipStream_t stream) {
+    const PagedKV none{nullptr, nullptr, 0, 0, 0};
+    hipError_t e = launch_typed<D, CAUSAL, false, false, 1>(q, k, v, o, lse, B, H, Hkv, Nq, Nk,
+                                                            scale, none, stream);
+    if (e != hipSuccess) return e;
+    return launch_typed<D, CAUSAL, false, false, 2>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale,
+                                                    none, stream);
+}
+
+hipError_t launch_fwd_bf16_two_pass(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, int B, int H, int Hkv, int Nq, int Nk, int d,
+                                    int causal, float scale, hipStream_t stream) {
+    if (d == 128)
+        return causal ? launch_two_pass<128, true>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream)
+                      : launch_two_pass<128, false>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream);
+    return causal ? launch_two_pass<64, true>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream)
+                  : launch_two_pass<64, false>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream);
 }
 
 hipError_t launch_fwd_bf16_paged(const void* q, const void* k_cache, const void* v_cache,

@@ -18,5 +18,6 @@ from .attention import (  # noqa: F401
     online_softmax_stats,
     scatter_pages,
     softmax_rows,
+    two_pass_attention_row,
     window_mask,
 )

@@ -262,6 +262,29 @@ def online_attention_row(scores_row, v, block_sizes):
     return acc / L, M + math.log(L)
 
 
+def two_pass_attention_row(scores_row, v, block_sizes):
+    """FlashAttention-1's two passes over one row's key blocks, in float64.
+
+    Page "Donanıma Duyarlı Algoritma Tasarımı: FlashAttention", section
+    "FlashAttention-1 (İki Geçişli Yaklaşım)": the first pass runs the online softmax
+    over the blocks and keeps only the row's global max M and sum L
+    (``online_softmax_stats``); the second pass recomputes each block's scores,
+    normalises them with M and L (exp(s - M) / L) and accumulates them times the
+    block's V rows. ``scores_row`` holds only the row's attended keys (masked keys
+    dropped) and v their value rows. Returns (o, lse = M + ln L).
+    """
+    s = np.asarray(scores_row, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    M, L = online_softmax_stats(s, block_sizes)       # pass 1: statistics only
+    acc = np.zeros(v.shape[1])
+    pos = 0
+    for bs in block_sizes:                            # pass 2: normalised blocks
+        p = np.exp(s[pos:pos + bs] - M) / L
+        acc = acc + p @ v[pos:pos + bs]
+        pos += bs
+    return acc, M + math.log(L)
+
+
 def merge_partials(o_parts, lse_parts):
     """Combine attention results over disjoint key sets by their log-sum-exps.
 

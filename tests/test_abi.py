@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert set(declared_functions()) == {
         "fa_fwd", "fa_fwd_fp32", "fa_decode_paged", "fa_decode_paged_workspace_size",
-        "fa_decode_paged_split_tokens", "fa_fwd_paged", "fa_kv_append", "fa_fwd_window", "fa_status_string"}
+        "fa_decode_paged_split_tokens", "fa_fwd_paged", "fa_kv_append", "fa_fwd_window", "fa_fwd_two_pass", "fa_status_string"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -50,12 +50,17 @@ def test_status_strings(lib):
     assert _lib.fa_status_string(-1).startswith("FA_ERR_INVALID")
 
 
-def _fwd(lib, fn="fa_fwd", q=P, k=P, v=P, o=P, lse=None, B=1, H=8, Hkv=8, Nq=64, Nk=64, d=128,
+def _fwd(lib, fn="fa_fwd", q=P, k=P, v=P, o=P, lse=P, B=1, H=8, Hkv=8, Nq=64, Nk=64, d=128,
          causal=1, scale=0.125):
     return getattr(lib, fn)(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale, None)
 
 
-@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_fp32"])
+def test_two_pass_requires_lse(lib):
+    assert lib.fa_fwd_two_pass(P, P, P, P, None, 1, 8, 8, 64, 64, 128, 1, 0.125, None) == INVALID
+    assert lib.fa_fwd_two_pass(P, P, P, P, P, 1, 8, 8, 64, 64, 96, 1, 0.125, None) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_fp32", "fa_fwd_two_pass"])
 @pytest.mark.parametrize("kw,want", [
     (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(k=P + 8), INVALID),
     (dict(lse=P + 2), INVALID),

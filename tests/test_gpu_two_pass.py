@@ -1,0 +1,73 @@
+"""GPU parity of the FlashAttention-1 two-pass prefill (fa_fwd_two_pass).
+
+Page "Donanıma Duyarlı Algoritma Tasarımı: FlashAttention", section "FlashAttention-1
+(İki Geçişli Yaklaşım)": a statistics pass writes each row's (M, L) (here as lse) and an
+output pass renormalises recomputed scores with them. Checked against the fp64 oracle,
+and against the single-pass kernel: the statistics pass runs the single pass's
+arithmetic without the P.V products, so its lse must match fa_fwd's bit for bit, and the
+two outputs must agree to the bf16 bar.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_fa_amd import _lib, inputs
+from gpu_helpers import BF16_MAX_ABS, bf16_from_dev, bf16_to_dev, check_bf16, errors
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_both(inp):
+    import torch
+    c = inp.cfg
+    q, k, v = (bf16_to_dev(x) for x in (inp.q, inp.k, inp.v))
+    o2, o1 = torch.empty_like(q), torch.empty_like(q)
+    l2 = torch.empty((c.B, c.H, c.Nq), dtype=torch.float32, device="cuda")
+    l1 = torch.empty_like(l2)
+    _lib.fa_fwd_two_pass(q, k, v, o2, l2, causal=c.causal, scale=c.scale)
+    _lib.fa_fwd(q, k, v, o1, l1, causal=c.causal, scale=c.scale)
+    torch.cuda.synchronize()
+    return bf16_from_dev(o2), l2.cpu().numpy(), bf16_from_dev(o1), l1.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d,causal", [
+    (2, 8, 2, 700, 700, 128, True),
+    (2, 8, 8, 513, 1000, 128, True),     # Nq < Nk, ragged
+    (1, 4, 1, 300, 450, 128, False),
+    (2, 8, 2, 1024, 1024, 64, True),     # d = 64
+    (1, 2, 2, 1, 77, 128, True),         # one query
+], ids=lambda x: str(x))
+def test_two_pass_vs_oracle_and_single_pass(B, H, Hkv, Nq, Nk, d, causal):
+    inp = inputs.custom_prefill(B, H, Hkv, Nq, Nk, d, causal, seed=Nq + Nk + d)
+    _say(f"[two-pass] B{B} H{H} Hkv{Hkv} Nq{Nq} Nk{Nk} d{d} causal={causal}")
+    o2, l2, o1, l1 = run_both(inp)
+    q, k, v = inp.as_f64()
+    O, L = oracle.attention(q, k, v, causal=causal, scale=inp.cfg.scale)
+    check_bf16(inputs.bf16_bits_to_f64(o2), l2, O, L, "two-pass vs oracle")
+    assert np.array_equal(l2, l1), "statistics pass lse differs from the single pass"
+    mx, _ = errors(inputs.bf16_bits_to_f64(o2), inputs.bf16_bits_to_f64(o1))
+    assert mx <= BF16_MAX_ABS, f"two-pass vs single-pass max-abs {mx}"
+
+
+def test_two_pass_gqa_sampled():
+    """B4 H32 Hkv8 N4096 d128 causal; rows sampled for the oracle."""
+    cfg = inputs.PREFILL_CONFIGS["gqa_causal"]
+    inp = inputs.make_prefill(cfg)
+    _say("[two-pass] gqa_causal sampled")
+    o2, l2, o1, l1 = run_both(inp)
+    assert np.array_equal(l2, l1)
+    rows = inputs.sample_rows(inp, 1, 128)
+    q, k, v = inp.as_f64()
+    O, L = oracle.attention(q, k, v, causal=True, scale=cfg.scale, rows=rows)
+    got = np.concatenate([inputs.bf16_bits_to_f64(o2[b, h, idx]) for (b, h), idx in rows.items()])
+    want = np.concatenate([O[key] for key in rows])
+    gl = np.concatenate([l2[b, h, idx] for (b, h), idx in rows.items()])
+    wl = np.concatenate([L[key] for key in rows])
+    check_bf16(got, gl, want, wl, "two-pass gqa sampled")

@@ -5,6 +5,8 @@ import numpy as np
 import pytest
 
 import oracle
+from scipy.special import logsumexp as scipy_logsumexp
+from scipy.special import softmax as scipy_softmax
 from oracle.brute import attention_brute
 from kv_cache_fa_amd import inputs
 from pins import ALL_PINS, load_golden, parse_arr, parse_num
@@ -176,6 +178,34 @@ def test_gather_pages_detects_a_wrong_slot():
     t = np.arange(L)
     wrong = inp.k_cache[inp.page_table[s, t // 16], (t + 1) % 16]
     assert not np.array_equal(wrong, inp.k_seq[s])
+
+
+# ---- FlashAttention-1 two passes ---------------------------------------------------
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_two_pass_equals_definition(seed):
+    """Statistics pass + normalised output pass = softmax(s) @ v, any blocking."""
+    rng = np.random.default_rng(seed)
+    n, d = 37, 5
+    s = rng.standard_normal(n) * 3
+    v = rng.standard_normal((n, d))
+    cuts = sorted(rng.choice(np.arange(1, n), size=4, replace=False))
+    blocks = np.diff([0, *cuts, n]).tolist()
+    o, lse = oracle.two_pass_attention_row(s, v, blocks)
+    p = scipy_softmax(s)
+    np.testing.assert_allclose(o, p @ v, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, scipy_logsumexp(s), rtol=0, atol=1e-13)
+
+
+def test_two_pass_statistics_are_the_golden_trace():
+    """Pass 1 keeps exactly the page's (M, L) for the hand-worked row."""
+    g = load_golden("online_softmax.json")
+    for case in g["stats"]:
+        s = parse_arr(case["scores"])
+        M, L = parse_num(case["M"]), parse_num(case["L"])
+        o, lse = oracle.two_pass_attention_row(s, np.eye(len(s)), case["blocks"])
+        np.testing.assert_allclose(lse, M + math.log(L), rtol=0, atol=1e-14)
+        # V = I, so o is the probability row: [1, 2, 4] / 7
+        np.testing.assert_allclose(o, np.array([1, 2, 4]) / 7, rtol=0, atol=1e-14)
 
 
 # ---- sliding window (glossary entry "Kayan Pencere Dikkati") -----------------------
