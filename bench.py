@@ -340,6 +340,25 @@ def main(argv=None):
             "frac_of_bf16_peak": round(w_tf / PEAK_BF16_TFLOPS, 4)}
         del wq, wk, wv, wo, wlse
 
+        # Paged decode on an fp8 (e4m3) copy of the decode workload's cache.
+        log("[bench] extra: fp8 paged decode")
+        f8 = inputs.quantize_decode_fp8(dinp)
+        fkc = torch.from_numpy(f8.k_cache).to(dev)
+        fvc = torch.from_numpy(f8.v_cache).to(dev)
+        fks = torch.from_numpy(f8.k_scale).to(dev)
+        fvs = torch.from_numpy(f8.v_scale).to(dev)
+        f_ms = timed(lambda: _lib.fa_decode_paged_fp8(dq, fkc, fvc, fks, fvs, dpt, dsl, do, dlse,
+                                                      max_seq_len=dcfg.max_seq_len,
+                                                      scale=dcfg.scale, workspace=ws,
+                                                      stream=stream))
+        f_bytes = decode_bytes(dinp) - dinp.kv_bytes() // 2  # K/V bytes halve, the rest stays
+        f_gbs = f_bytes / (f_ms * 1e-3) / 1e9
+        out["legs"]["decode_fp8"] = {
+            "bytes": f_bytes, "ms_mean": round(f_ms, 4), "GB/s": round(f_gbs, 1),
+            "frac_of_hbm_peak": round(f_gbs / PEAK_HBM_GBS, 4),
+            "tokens_per_s": round(float(dinp.seq_lens.sum()) / (f_ms * 1e-3), 1)}
+        del fkc, fvc, fks, fvs
+
         # KV append of that chunk size: 8 sequences x 1024 new tokens into a cache
         # with room for 16384 tokens each.
         log("[bench] extra: kv append")

@@ -137,6 +137,27 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                     int num_pages, int max_pages_per_seq, int max_seq_len, float scale,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_decode_paged_fp8 — fa_decode_paged on a cache stored in 8-bit floating point
+ * (glossary entry "KV Cache (Anahtar-Değer Önbelleği)": quantising the KV cache to
+ * INT8/FP8 cuts its memory 2-4x). Each cached element is one byte in the OCP e4m3 format
+ * (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, 0x7f/0xff
+ * NaN); its value is the decoded byte times the scale of its KV head:
+ *   k_cache, v_cache  [num_pages, page_size, Hkv, d] uint8 (e4m3)
+ *   k_scale, v_scale  [Hkv] fp32, device memory; finite and >= 0
+ * Everything else (q, o, lse, page_table, seq_lens, workspace and its size, errors,
+ * device-side behaviour) is as for fa_decode_paged. The result is the attention of the
+ * dequantised cache: bytes are converted exactly, scores and the softmax are fp32 and
+ * the K scale is folded into the softmax scale, the V scale into each split's output.
+ * k_scale or v_scale NULL or misaligned: FA_ERR_INVALID.
+ */
+int fa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
+                        const float* k_scale, const float* v_scale,
+                        const int32_t* page_table, const int32_t* seq_lens, int page_size,
+                        void* o, float* lse, int num_seqs, int H, int Hkv, int d,
+                        int num_pages, int max_pages_per_seq, int max_seq_len, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Tokens of KV one split-K work-group covers for these sizes (a multiple of the page
  * size); the workspace holds ceil(max_seq_len / split) partial results per head. */
 int fa_decode_paged_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size);

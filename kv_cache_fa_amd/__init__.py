@@ -10,6 +10,7 @@ call does, and raises if it has not been built.
 from ._lib import (  # noqa: F401
     KvfaError,
     fa_decode_paged,
+    fa_decode_paged_fp8,
     fa_decode_paged_split_tokens,
     fa_decode_paged_workspace_size,
     fa_fwd,

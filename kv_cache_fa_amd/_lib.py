@@ -31,6 +31,8 @@ SIGNATURES = {
     "fa_fwd_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                           _i, _f, _vp]),
     "fa_kv_append": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "fa_decode_paged_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i,
+                                 _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
 }
 
@@ -239,4 +241,36 @@ def fa_kv_append(k_new, v_new, k_cache, v_cache, page_table, start_pos, *, strea
     _check("fa_kv_append", lib().fa_kv_append(
         _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
         _ptr(start_pos), page_size, S, n_new, Hkv, d, num_pages, int(page_table.shape[1]),
+        _stream(stream)))
+
+
+def fa_decode_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens, o,
+                        lse=None, *, max_seq_len: int, scale: float, workspace, stream=None):
+    """Paged decode on an e4m3 cache. q,o [S,H,d] bf16; caches [P,16,Hkv,d] uint8 (e4m3
+    bytes); k_scale, v_scale [Hkv] fp32 (device); page_table [S,M] int32; seq_lens [S]."""
+    import torch
+    for t, n in ((q, "q"), (o, "o")):
+        _check_tensor(t, torch.bfloat16, n)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _check_tensor(t, torch.uint8, n)
+    for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        _check_tensor(t, torch.float32, n)
+    _check_tensor(page_table, torch.int32, "page_table")
+    _check_tensor(seq_lens, torch.int32, "seq_lens")
+    S, H, d = q.shape
+    num_pages, page_size, Hkv, dk = k_cache.shape
+    _require(dk == d and tuple(v_cache.shape) == tuple(k_cache.shape), "cache shape mismatch")
+    _require(tuple(k_scale.shape) == tuple(v_scale.shape) == (Hkv,), "scales must be [Hkv]")
+    _require(tuple(o.shape) == tuple(q.shape), "o must have q's shape")
+    _require(page_table.dim() == 2 and page_table.shape[0] == S, "page_table must be [S, M]")
+    _require(tuple(seq_lens.shape) == (S,), "seq_lens must be [S]")
+    if lse is not None:
+        _check_tensor(lse, torch.float32, "lse")
+        _require(tuple(lse.shape) == (S, H), "lse must be [S,H]")
+    _require(workspace.is_cuda and workspace.is_contiguous(), "workspace must be device memory")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("fa_decode_paged_fp8", lib().fa_decode_paged_fp8(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(page_table),
+        _ptr(seq_lens), page_size, _ptr(o), _ptr(lse), S, H, Hkv, d, num_pages,
+        int(page_table.shape[1]), int(max_seq_len), float(scale), _ptr(workspace), ws_bytes,
         _stream(stream)))

@@ -31,6 +31,13 @@ int check_prefill(const void* q, const void* k, const void* v, const void* o, co
     return FA_OK;
 }
 
+int decode_checked(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* page_table, const int32_t* seq_lens, int page_size, void* o,
+                   float* lse, int num_seqs, int H, int Hkv, int d, int num_pages,
+                   int max_pages_per_seq, int max_seq_len, float scale, void* workspace,
+                   size_t workspace_bytes, void* stream, const float* k_scale,
+                   const float* v_scale);
+
 }  // namespace
 
 extern "C" {
@@ -102,6 +109,20 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                     float* lse, int num_seqs, int H, int Hkv, int d, int num_pages,
                     int max_pages_per_seq, int max_seq_len, float scale, void* workspace,
                     size_t workspace_bytes, void* stream) {
+    return decode_checked(q, k_cache, v_cache, page_table, seq_lens, page_size, o, lse, num_seqs,
+                          H, Hkv, d, num_pages, max_pages_per_seq, max_seq_len, scale, workspace,
+                          workspace_bytes, stream, nullptr, nullptr);
+}
+
+}  // extern "C"
+
+namespace {
+int decode_checked(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* page_table, const int32_t* seq_lens, int page_size, void* o,
+                   float* lse, int num_seqs, int H, int Hkv, int d, int num_pages,
+                   int max_pages_per_seq, int max_seq_len, float scale, void* workspace,
+                   size_t workspace_bytes, void* stream, const float* k_scale,
+                   const float* v_scale) {
     if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !o || !workspace)
         return FA_ERR_INVALID;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
@@ -126,9 +147,12 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
     hipError_t e = kvfa::launch_decode_paged(q, k_cache, v_cache, page_table, seq_lens, o, lse,
                                              num_seqs, H, Hkv, d, num_pages, max_pages_per_seq,
                                              max_seq_len, scale, workspace,
-                                             static_cast<hipStream_t>(stream));
+                                             static_cast<hipStream_t>(stream), k_scale, v_scale);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
+}  // namespace
+
+extern "C" {
 
 int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
                  const int32_t* page_table, const int32_t* seq_lens, int page_size, void* o,
@@ -173,6 +197,19 @@ int fa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_ca
                                           num_seqs, n_new, Hkv, d, num_pages, max_pages_per_seq,
                                           static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
+                        const float* k_scale, const float* v_scale,
+                        const int32_t* page_table, const int32_t* seq_lens, int page_size,
+                        void* o, float* lse, int num_seqs, int H, int Hkv, int d,
+                        int num_pages, int max_pages_per_seq, int max_seq_len, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+        return FA_ERR_INVALID;
+    return decode_checked(q, k_cache, v_cache, page_table, seq_lens, page_size, o, lse, num_seqs,
+                          H, Hkv, d, num_pages, max_pages_per_seq, max_seq_len, scale, workspace,
+                          workspace_bytes, stream, k_scale, v_scale);
 }
 
 const char* fa_status_string(int status) {

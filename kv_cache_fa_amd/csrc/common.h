@@ -37,6 +37,32 @@ __device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2);
 }
 
+// 8 bytes per lane, nontemporal.
+__device__ __forceinline__ u32x2 buf_load8_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 2);
+}
+
+// ---- fp8 (OCP e4m3: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+// infinities, 0x7f / 0xff are NaN) ----------------------------------------------------
+// Every e4m3 value is exactly representable in bf16 and fp32, so these conversions are
+// exact (hardware conversion with a scale of 1).
+// Four e4m3 bytes (byte i = element i) -> four bf16 in two dwords.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+// Four e4m3 bytes -> four fp32.
+__device__ __forceinline__ void fp8x4_to_f32x4(uint32_t w, float* x) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    x[0] = lo[0];
+    x[1] = lo[1];
+    x[2] = hi[0];
+    x[3] = hi[1];
+}
+
 // 16 bytes per lane from a buffer straight into LDS: lane L writes lds_base + 16 L
 // (buffer_load_dwordx4 ... lds). lds_base must be the same in all lanes; loads past the
 // descriptor's size write zeros. The builtin only exists for the device, and naming it

@@ -21,6 +21,8 @@
 //   it through a small per-wave LDS table.
 // * The split's partial result (normalised O_k, lse_k in log2 units) goes to the
 //   caller's workspace; a second kernel merges the splits in order.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -31,14 +33,21 @@ namespace {
 constexpr int kPage = 16;
 constexpr int kWaves = 4;
 
-template <int D, int GH>
+// FP8 = true: the cache holds e4m3 bytes with one scale per KV head for K and one for V
+// (dequantised value = byte value x scale). K bytes are converted exactly to bf16 for the
+// MFMA and V bytes to fp32 for the P.V FMAs; the K scale is folded into the softmax
+// scale and the V scale is applied to the split's output, so the arithmetic is that of
+// the dequantised cache. Each cached token costs half the bytes of the bf16 cache.
+template <int D, int GH, bool FP8>
 __global__ __launch_bounds__(256) void decode_split_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kcache,
-    const uint16_t* __restrict__ vcache, const int32_t* __restrict__ page_table,
+    const uint16_t* __restrict__ q, const void* __restrict__ kcache,
+    const void* __restrict__ vcache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
     float* __restrict__ lse_part, int H, int Hkv, int g, int n_hg, int num_pages,
-    int max_pages, int max_seq_len, int split_tokens, int max_splits, float scale_log2,
-    float tau_raw) {
+    int max_pages, int max_seq_len, int split_tokens, int max_splits, float scale_log2_in,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+    constexpr int ES = FP8 ? 1 : 2;    // bytes per cached element
+    using KVec = std::conditional_t<FP8, u32x2, u32x4>;  // 8 cached elements
     constexpr int CH = D / 8;          // 16-byte chunks per token row
     constexpr int TG = 64 / CH;        // token groups of the P.V lane layout
     constexpr int TPL = kPage / TG;    // tokens per lane in P.V
@@ -67,6 +76,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const int h0 = kvh * g + hg * GH;
     const int nheads = min(GH, g - hg * GH);
     const size_t tok_stride = (size_t)Hkv * D;  // elements between consecutive slots
+    // Softmax scale in log2 units (times the K scale for an fp8 cache) and the V scale.
+    float scale_log2 = scale_log2_in, v_sc = 1.f;
+    if constexpr (FP8) {
+        scale_log2 *= k_scale[kvh];
+        v_sc = v_scale[kvh];
+    }
+    // Move the reference max past +8 in log2 units (with a zero K scale every score is 0:
+    // the first page then moves the reference and every later one keeps it).
+    const float tau_raw = scale_log2 > 0.f ? 8.0f / scale_log2 : 0.f;
 
     // B operand (Q^T): Q[s][h0+n][8*(4j + kq) .. +7], zero for padding columns.
     u32x4 qf[KS];
@@ -99,34 +117,45 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     // Loads are issued unconditionally (a zero-size descriptor for an invalid page id
     // makes them return zeros without touching memory), so the wait counts stay exact.
     // The cache is read once per call: the loads carry the nontemporal hint.
-    const uint32_t span = (uint32_t)((kPage - 1) * tok_stride + D) * 2;
-    const uint32_t k_off = (uint32_t)(n * tok_stride) * 2 + kq * 16;
-    const uint32_t v_off = (uint32_t)(tg * tok_stride + c * 8) * 2;
-    auto load_page = [&](int it, u32x4 (&kf)[KS], u32x4 (&vv)[TPL]) -> bool {
+    const uint32_t span = (uint32_t)((kPage - 1) * tok_stride + D) * ES;
+    const uint32_t k_off = (uint32_t)(n * tok_stride + kq * 8) * ES;
+    const uint32_t v_off = (uint32_t)(tg * tok_stride + c * 8) * ES;
+    auto load8 = [&](__amdgpu_buffer_rsrc_t r, uint32_t off) -> KVec {
+        if constexpr (FP8) return buf_load8_nt(r, off);
+        else return buf_load16_nt(r, off);
+    };
+    auto load_page = [&](int it, KVec (&kf)[KS], KVec (&vv)[TPL]) -> bool {
         const int pid = __builtin_amdgcn_readlane(pid_lane, it);
         const bool valid = (unsigned)pid < (unsigned)num_pages;
         const size_t page_base = (size_t)(valid ? pid : 0) * kPage * tok_stride + (size_t)kvh * D;
-        const auto rk = make_rsrc(kcache + page_base, valid ? span : 0u);
-        const auto rv = make_rsrc(vcache + page_base, valid ? span : 0u);
+        const auto rk = make_rsrc(static_cast<const char*>(kcache) + page_base * ES, valid ? span : 0u);
+        const auto rv = make_rsrc(static_cast<const char*>(vcache) + page_base * ES, valid ? span : 0u);
 #pragma unroll
-        for (int j = 0; j < KS; ++j) kf[j] = buf_load16_nt(rk, k_off + j * 64);
+        for (int j = 0; j < KS; ++j) kf[j] = load8(rk, k_off + j * 32 * ES);
 #pragma unroll
         for (int i = 0; i < TPL; ++i)
-            vv[i] = buf_load16_nt(rv, v_off + (uint32_t)(TG * i * tok_stride) * 2);
+            vv[i] = load8(rv, v_off + (uint32_t)(TG * i * tok_stride) * ES);
         return valid;
     };
 
-    u32x4 kA[KS], vA[TPL], kB[KS], vB[TPL];
+    KVec kA[KS], vA[TPL], kB[KS], vB[TPL];
     bool okA = load_page(0, kA, vA);   // a lane past the wave's pages holds id -1
     bool okB = false;
-    auto page_compute = [&](const u32x4 (&KF)[KS], const u32x4 (&VV)[TPL], const bool OK, const int IT) {
+    auto page_compute = [&](const KVec (&KF)[KS], const KVec (&VV)[TPL], const bool OK, const int IT) {
         if (OK) {
             const int tok0 = (first_page + w + kWaves * IT) * kPage;
 
             // S^T: acc[i] = score of token 4*kq + i for head column n
             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < KS; ++j) acc = mfma16x16x32(KF[j], qf[j], acc);
+            for (int j = 0; j < KS; ++j) {
+                if constexpr (FP8) {
+                    const u32x2 lo = fp8x4_to_bf16x4(KF[j][0]), hi = fp8x4_to_bf16x4(KF[j][1]);
+                    acc = mfma16x16x32(u32x4{lo[0], lo[1], hi[0], hi[1]}, qf[j], acc);
+                } else {
+                    acc = mfma16x16x32(KF[j], qf[j], acc);
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (tok0 + kq * 4 + i >= t1) acc[i] = -INFINITY;
@@ -139,7 +168,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
             const bool resc = __builtin_amdgcn_ballot_w64(move) != 0;
             if (resc) {
                 const float m_new = move ? m_cand : m_used;  // alpha = 1 for unmoved heads
-                const float alpha = fast_exp2((m_used - m_new) * scale_log2);
+                const float alpha = move ? fast_exp2((m_used - m_new) * scale_log2) : 1.f;
                 m_used = m_new;
                 l_part *= alpha;
                 if (kq == 0 && n < GH) a_lds[w][n] = alpha;
@@ -166,11 +195,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
                 const int tl = tg + TG * i;
                 const bool ok = tok0 + tl < t1;  // slots past the sequence may hold anything
                 float x[8];
+                if constexpr (FP8) {
+                    fp8x4_to_f32x4(ok ? VV[i][0] : 0u, x);
+                    fp8x4_to_f32x4(ok ? VV[i][1] : 0u, x + 4);
+                } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t wd = ok ? VV[i][e] : 0u;
-                    x[2 * e] = bf16lo(wd);
-                    x[2 * e + 1] = bf16hi(wd);
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t wd = ok ? VV[i][e] : 0u;
+                        x[2 * e] = bf16lo(wd);
+                        x[2 * e + 1] = bf16hi(wd);
+                    }
                 }
 #pragma unroll
                 for (int hh = 0; hh < GH; ++hh) {
@@ -223,13 +257,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         if (M != -INFINITY) {
 #pragma unroll
             for (int ww = 0; ww < kWaves; ++ww) {
-                const float f = fast_exp2((red_m[ww][hh] - M) * scale_log2);  // 0 for empty waves
+                const float mw = red_m[ww][hh];  // -inf for a wave that saw no token
+                const float f = mw == -INFINITY ? 0.f : fast_exp2((mw - M) * scale_log2);
                 lsum = fmaf(f, red_l[ww][hh], lsum);
                 acc = fmaf(f, red_o[ww][hh][dd], acc);
             }
         }
         const size_t row = ((size_t)s * H + h0 + hh) * max_splits + split;
-        o_part[row * D + dd] = M != -INFINITY ? acc / lsum : 0.f;
+        o_part[row * D + dd] = M != -INFINITY ? acc / lsum * v_sc : 0.f;
         if (dd == 0)
             lse_part[row] = M != -INFINITY ? M * scale_log2 + fast_log2(lsum) : -INFINITY;
     }
@@ -289,42 +324,41 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
         lse[row] = M != -INFINITY ? (M + fast_log2(W)) * kLn2 : -INFINITY;
 }
 
-template <int D, int GH>
+template <int D, int GH, bool FP8>
 hipError_t launch_split(const void* q, const void* kc, const void* vc, const int32_t* pt,
                         const int32_t* sl, float* o_part, float* lse_part, int num_seqs, int H,
                         int Hkv, int g, int n_hg, int num_pages, int max_pages, int max_seq_len,
-                        int split_tokens, int max_splits, float scale, hipStream_t stream) {
+                        int split_tokens, int max_splits, float scale, const float* k_scale,
+                        const float* v_scale, hipStream_t stream) {
     const float scale_log2 = scale * kLog2e;
-    const float tau_raw = 8.0f / scale_log2;
     // KV heads vary fastest: the work-groups covering one token range of one sequence
     // are dispatched together, so each physical page (all KV heads of 16 slots, contiguous)
     // is read by concurrently running work-groups.
     dim3 grid(Hkv * n_hg, max_splits, num_seqs);
-    hipLaunchKernelGGL((decode_split_kernel<D, GH>), grid, dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-                       static_cast<const uint16_t*>(vc), pt, sl, o_part, lse_part, H, Hkv, g,
-                       n_hg, num_pages, max_pages, max_seq_len, split_tokens, max_splits,
-                       scale_log2, tau_raw);
+    hipLaunchKernelGGL((decode_split_kernel<D, GH, FP8>), grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), kc, vc, pt, sl, o_part, lse_part, H, Hkv,
+                       g, n_hg, num_pages, max_pages, max_seq_len, split_tokens, max_splits,
+                       scale_log2, k_scale, v_scale);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool FP8>
 hipError_t launch_split_d(int GH, const void* q, const void* kc, const void* vc,
                           const int32_t* pt, const int32_t* sl, float* o_part, float* lse_part,
                           int num_seqs, int H, int Hkv, int g, int n_hg, int num_pages,
                           int max_pages, int max_seq_len, int split_tokens, int max_splits,
-                          float scale, hipStream_t stream) {
+                          float scale, const float* ks, const float* vs, hipStream_t stream) {
     if (GH == 4)
-        return launch_split<D, 4>(q, kc, vc, pt, sl, o_part, lse_part, num_seqs, H, Hkv, g, n_hg,
-                                  num_pages, max_pages, max_seq_len, split_tokens, max_splits,
-                                  scale, stream);
+        return launch_split<D, 4, FP8>(q, kc, vc, pt, sl, o_part, lse_part, num_seqs, H, Hkv, g,
+                                       n_hg, num_pages, max_pages, max_seq_len, split_tokens,
+                                       max_splits, scale, ks, vs, stream);
     if (GH == 8)
-        return launch_split<D, 8>(q, kc, vc, pt, sl, o_part, lse_part, num_seqs, H, Hkv, g, n_hg,
-                                  num_pages, max_pages, max_seq_len, split_tokens, max_splits,
-                                  scale, stream);
-    return launch_split<D, 16>(q, kc, vc, pt, sl, o_part, lse_part, num_seqs, H, Hkv, g, n_hg,
-                               num_pages, max_pages, max_seq_len, split_tokens, max_splits,
-                               scale, stream);
+        return launch_split<D, 8, FP8>(q, kc, vc, pt, sl, o_part, lse_part, num_seqs, H, Hkv, g,
+                                       n_hg, num_pages, max_pages, max_seq_len, split_tokens,
+                                       max_splits, scale, ks, vs, stream);
+    return launch_split<D, 16, FP8>(q, kc, vc, pt, sl, o_part, lse_part, num_seqs, H, Hkv, g,
+                                    n_hg, num_pages, max_pages, max_seq_len, split_tokens,
+                                    max_splits, scale, ks, vs, stream);
 }
 
 }  // namespace
@@ -352,7 +386,9 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
                                const int32_t* page_table, const int32_t* seq_lens, void* o,
                                float* lse, int num_seqs, int H, int Hkv, int d, int num_pages,
                                int max_pages_per_seq, int max_seq_len, float scale,
-                               void* workspace, hipStream_t stream) {
+                               void* workspace, hipStream_t stream, const float* k_scale,
+                               const float* v_scale) {
+    const bool fp8 = k_scale != nullptr;
     const int T = decode_split_tokens(num_seqs, Hkv, max_seq_len, kPage);
     const int max_splits = (max_seq_len + T - 1) / T;
     const int g = H / Hkv;
@@ -361,13 +397,25 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
     float* o_part = static_cast<float*>(workspace);
     float* lse_part = o_part + (size_t)num_seqs * H * max_splits * d;
 
-    hipError_t e = d == 128
-        ? launch_split_d<128>(GH, q, k_cache, v_cache, page_table, seq_lens, o_part, lse_part,
-                              num_seqs, H, Hkv, g, n_hg, num_pages, max_pages_per_seq,
-                              max_seq_len, T, max_splits, scale, stream)
-        : launch_split_d<64>(GH, q, k_cache, v_cache, page_table, seq_lens, o_part, lse_part,
-                             num_seqs, H, Hkv, g, n_hg, num_pages, max_pages_per_seq,
-                             max_seq_len, T, max_splits, scale, stream);
+    hipError_t e;
+    if (d == 128)
+        e = fp8 ? launch_split_d<128, true>(GH, q, k_cache, v_cache, page_table, seq_lens, o_part,
+                                            lse_part, num_seqs, H, Hkv, g, n_hg, num_pages,
+                                            max_pages_per_seq, max_seq_len, T, max_splits, scale,
+                                            k_scale, v_scale, stream)
+                : launch_split_d<128, false>(GH, q, k_cache, v_cache, page_table, seq_lens,
+                                             o_part, lse_part, num_seqs, H, Hkv, g, n_hg,
+                                             num_pages, max_pages_per_seq, max_seq_len, T,
+                                             max_splits, scale, nullptr, nullptr, stream);
+    else
+        e = fp8 ? launch_split_d<64, true>(GH, q, k_cache, v_cache, page_table, seq_lens, o_part,
+                                           lse_part, num_seqs, H, Hkv, g, n_hg, num_pages,
+                                           max_pages_per_seq, max_seq_len, T, max_splits, scale,
+                                           k_scale, v_scale, stream)
+                : launch_split_d<64, false>(GH, q, k_cache, v_cache, page_table, seq_lens,
+                                            o_part, lse_part, num_seqs, H, Hkv, g, n_hg,
+                                            num_pages, max_pages_per_seq, max_seq_len, T,
+                                            max_splits, scale, nullptr, nullptr, stream);
     if (e != hipSuccess) return e;
     dim3 grid((H + kCombineHeads - 1) / kCombineHeads, num_seqs);
     if (d == 128)

@@ -46,6 +46,7 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
                                const int32_t* page_table, const int32_t* seq_lens, void* o,
                                float* lse, int num_seqs, int H, int Hkv, int d, int num_pages,
                                int max_pages_per_seq, int max_seq_len, float scale,
-                               void* workspace, hipStream_t stream);
+                               void* workspace, hipStream_t stream,
+                               const float* k_scale = nullptr, const float* v_scale = nullptr);
 
 }  // namespace kvfa

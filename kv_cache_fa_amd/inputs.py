@@ -68,6 +68,43 @@ def bf16_bits_to_f64(u: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------
+# fp8 storage (OCP e4m3: sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+# infinities; 0x7f and 0xff are NaN; largest finite magnitude 448)
+# ----------------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_to_f64(u: np.ndarray) -> np.ndarray:
+    """Decode e4m3 bytes to float64 exactly, from the format's definition."""
+    u = np.asarray(u, dtype=np.uint8).astype(np.int64)
+    sign = np.where(u & 0x80, -1.0, 1.0)
+    e = (u >> 3) & 0xF
+    m = (u & 7).astype(np.float64)
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7))
+    val = sign * val
+    return np.where((e == 15) & ((u & 7) == 7), np.nan, val)
+
+
+_E4M3_FINITE = np.array([b for b in range(128) if b != 0x7F], dtype=np.uint8)
+
+
+def f64_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest e4m3 value, ties to the even code, saturating at +-448 (finite
+    inputs only). Nearest is found among the 127 non-negative finite codes by search."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("e4m3 encoding expects finite values")
+    mags = e4m3_to_f64(_E4M3_FINITE)            # increasing with the code
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, len(mags) - 1)
+    lo = np.clip(hi - 1, 0, len(mags) - 1)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (_E4M3_FINITE[hi] % 2 == 0))
+    code = np.where(pick_hi, _E4M3_FINITE[hi], _E4M3_FINITE[lo]).astype(np.uint8)
+    return np.where((x < 0) & (code != 0), code | 0x80, code).astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------------
 # Prefill workloads
 # ----------------------------------------------------------------------------------
 @dataclasses.dataclass(frozen=True)
@@ -372,3 +409,41 @@ def make_append(S, n_new, Hkv, d, max_seq_len, *, page_size=16, seed=0, start_po
     k_new = _draw(rng, (S, n_new, Hkv, d), 1.0, "bf16")
     v_new = _draw(rng, (S, n_new, Hkv, d), 1.0, "bf16")
     return AppendInputs(k_cache, v_cache, table, start_pos, k_new, v_new)
+
+
+@dataclasses.dataclass
+class DecodeFp8Inputs:
+    base: DecodeInputs       # the bf16 workload the fp8 cache was quantised from
+    k_cache: np.ndarray      # [num_pages,16,Hkv,d] uint8 e4m3
+    v_cache: np.ndarray
+    k_scale: np.ndarray      # [Hkv] float32
+    v_scale: np.ndarray
+    k_seq: list              # per sequence [L_s,Hkv,d] uint8, quantised before paging
+    v_seq: list
+
+
+def quantize_decode_fp8(base: DecodeInputs) -> DecodeFp8Inputs:
+    """Per KV head: scale = max |value| over every cached token / 448, bytes = e4m3(value /
+    scale). Slots past a sequence keep their fill (0 stays 0; NaN fill becomes 0x7f)."""
+    Hkv = base.cfg.Hkv
+
+    def quant(cache, seqs):
+        vals = bf16_bits_to_f64(cache)
+        amax = np.zeros(Hkv)
+        for x in seqs:
+            if x.shape[0]:
+                amax = np.maximum(amax, np.abs(bf16_bits_to_f64(x)).max(axis=(0, 2)))
+        sc = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32)
+        fin = np.isfinite(vals)
+        q = f64_to_e4m3(np.where(fin, vals / sc[None, None, :, None].astype(np.float64), 0.0))
+        q = np.where(fin, q, np.uint8(0x7F)).astype(np.uint8)
+        return q, sc
+
+    kq, ks = quant(base.k_cache, base.k_seq)
+    vq, vs = quant(base.v_cache, base.v_seq)
+
+    def quant_seq(x, sc):
+        return f64_to_e4m3(bf16_bits_to_f64(x) / sc[None, :, None].astype(np.float64))
+
+    return DecodeFp8Inputs(base, kq, vq, ks, vs, [quant_seq(x, ks) for x in base.k_seq],
+                           [quant_seq(x, vs) for x in base.v_seq])

@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert set(declared_functions()) == {
         "fa_fwd", "fa_fwd_fp32", "fa_decode_paged", "fa_decode_paged_workspace_size",
-        "fa_decode_paged_split_tokens", "fa_fwd_paged", "fa_kv_append", "fa_fwd_window", "fa_fwd_two_pass", "fa_status_string"}
+        "fa_decode_paged_split_tokens", "fa_fwd_paged", "fa_kv_append", "fa_fwd_window", "fa_fwd_two_pass", "fa_decode_paged_fp8", "fa_status_string"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -150,6 +150,25 @@ def _append(lib, kn=P, vn=P, kc=P, vc=P, pt=P, sp=P, page_size=16, S=4, n_new=8,
 ])
 def test_kv_append_validation(lib, kw, want):
     assert _append(lib, **kw) == want
+
+
+def test_decode_fp8_validation(lib):
+    ws = lib.fa_decode_paged_workspace_size(4, 32, 8, 128, 128, 16)
+
+    def call(ks=P, vs=P, **kw):
+        a = dict(q=P, kc=P, vc=P, pt=P, sl=P, page_size=16, o=P, lse=None, S=4, H=32, Hkv=8,
+                 d=128, num_pages=100, max_pages=8, max_seq_len=128, scale=0.09)
+        a.update(kw)
+        return lib.fa_decode_paged_fp8(a["q"], a["kc"], a["vc"], ks, vs, a["pt"], a["sl"],
+                                       a["page_size"], a["o"], a["lse"], a["S"], a["H"],
+                                       a["Hkv"], a["d"], a["num_pages"], a["max_pages"],
+                                       a["max_seq_len"], a["scale"], P, ws, None)
+    assert call(ks=None) == INVALID
+    assert call(vs=None) == INVALID
+    assert call(ks=P + 2) == INVALID
+    assert call(S=0) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(H=32, Hkv=5) == INVALID
 
 
 def test_workspace_size(lib):

@@ -1,0 +1,93 @@
+"""GPU parity of paged decode on an fp8 (e4m3) KV cache (fa_decode_paged_fp8).
+
+The oracle attends the dequantised values (byte value x per-head scale) of each
+sequence's K/V, quantised from the contiguous sequence before it was paged, so the
+kernel's page walk and byte conversion are both checked against an independent path.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_fa_amd import _lib, inputs
+from gpu_helpers import bf16_from_dev, bf16_to_dev, check_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_fp8(f: inputs.DecodeFp8Inputs):
+    import torch
+    b = f.base
+    c = b.cfg
+    q = bf16_to_dev(b.q)
+    kc = torch.from_numpy(f.k_cache).cuda()
+    vc = torch.from_numpy(f.v_cache).cuda()
+    ks = torch.from_numpy(f.k_scale).cuda()
+    vs = torch.from_numpy(f.v_scale).cuda()
+    pt = torch.from_numpy(b.page_table).cuda()
+    sl = torch.from_numpy(b.seq_lens).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((c.num_seqs, c.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(_lib.fa_decode_paged_workspace_size(c.num_seqs, c.H, c.Hkv, c.d,
+                                                         c.max_seq_len), dtype=torch.uint8,
+                     device="cuda")
+    _lib.fa_decode_paged_fp8(q, kc, vc, ks, vs, pt, sl, o, lse, max_seq_len=c.max_seq_len,
+                             scale=c.scale, workspace=ws)
+    torch.cuda.synchronize()
+    return bf16_from_dev(o), lse.cpu().numpy()
+
+
+def oracle_fp8(f: inputs.DecodeFp8Inputs):
+    b = f.base
+    ks = [inputs.e4m3_to_f64(x) * f.k_scale[None, :, None] for x in f.k_seq]
+    vs = [inputs.e4m3_to_f64(x) * f.v_scale[None, :, None] for x in f.v_seq]
+    return oracle.decode(inputs.bf16_bits_to_f64(b.q), ks, vs, scale=b.cfg.scale)
+
+
+def _check(f, what):
+    c = f.base.cfg
+    _say(f"[decode fp8] {what}: S{c.num_seqs} H{c.H} Hkv{c.Hkv} d{c.d}")
+    o_h, lse_h = run_fp8(f)
+    O, L = oracle_fp8(f)
+    check_bf16(inputs.bf16_bits_to_f64(o_h), lse_h, O, L, what)
+    return o_h, lse_h
+
+
+def test_fp8_paged_decode_full():
+    """64 sequences, H32/Hkv8, d128, lengths U{512..8192}, all rows."""
+    base = inputs.make_decode(inputs.DECODE_CONFIGS["paged_decode"])
+    _check(inputs.quantize_decode_fp8(base), "fp8 paged_decode")
+
+
+@pytest.mark.parametrize("S,H,Hkv,d,lo,hi", [
+    (5, 8, 8, 128, 1, 40),
+    (3, 32, 4, 128, 100, 3000),
+    (4, 16, 1, 128, 2000, 2100),
+    (2, 64, 2, 128, 10, 300),
+    (9, 32, 8, 64, 1, 1500),
+], ids=lambda x: str(x))
+def test_fp8_decode_shapes(S, H, Hkv, d, lo, hi):
+    base = inputs.custom_decode(S, H, Hkv, d, lo, hi, seed=7 * S + H + d)
+    _check(inputs.quantize_decode_fp8(base), f"fp8 S{S} H{H} Hkv{Hkv} d{d}")
+
+
+def test_fp8_edge_lengths_and_nan_slots():
+    """Empty sequence, page boundaries; unused slots hold e4m3 NaN bytes and the table is
+    padded with -1: the output must equal the zero-filled cache's bit for bit."""
+    cfg = inputs.DecodeConfig("edges", 8, 8, 2, 128, 0, 0, 16, 600, 1 / math.sqrt(128), 3)
+    lens = [0, 1, 15, 16, 17, 64, 65, 600]
+    a = inputs.quantize_decode_fp8(inputs.make_decode(cfg, seq_lens=lens))
+    b = inputs.quantize_decode_fp8(inputs.make_decode(cfg, seq_lens=lens, unused_fill="nan",
+                                                      table_pad=-1))
+    assert np.array_equal(a.k_scale, b.k_scale)
+    oa, la = _check(a, "fp8 edges")
+    ob, lb = run_fp8(b)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+    assert np.all(inputs.bf16_bits_to_f32(oa[0]) == 0.0) and np.all(la[0] == -np.inf)

@@ -115,3 +115,48 @@ def test_window_pairs_matches_the_mask():
             m &= j <= i + right
         assert inputs.window_pairs(Nq, Nk, left, right) == int(m.sum())
     assert inputs.window_pairs(6, 6, -1, 0) == inputs.unmasked_pairs(6, 6, True)
+
+
+# ---- e4m3 codec (OCP fp8: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits) ----
+def test_e4m3_known_codes():
+    codes = np.array([0x00, 0x01, 0x07, 0x08, 0x38, 0x39, 0x3F, 0x7E, 0xC0, 0xFE, 0x80])
+    want = [0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.125, 1.875, 448.0, -2.0, -448.0,
+            -0.0]
+    np.testing.assert_array_equal(inputs.e4m3_to_f64(codes), want)
+    assert np.isnan(inputs.e4m3_to_f64(np.array([0x7F, 0xFF]))).all()
+
+
+def test_e4m3_encode_is_nearest_with_ties_to_even_and_saturates():
+    finite = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = inputs.e4m3_to_f64(finite)
+    # every finite code round-trips (-0 encodes as +0)
+    back = inputs.f64_to_e4m3(vals)
+    assert np.array_equal(inputs.e4m3_to_f64(back), vals)
+    # brute force: random values map to the nearest code, ties to the even code
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(2000) * 30, rng.standard_normal(500) * 0.01,
+                        (vals[:-1] + vals[1:])[::7] / 2])       # some exact midpoints
+    enc = inputs.e4m3_to_f64(inputs.f64_to_e4m3(x))
+    for xi, ei in zip(x, enc):
+        d = np.abs(vals - min(max(xi, -448.0), 448.0))
+        best = vals[d == d.min()]
+        assert ei in best
+        if len(set(best)) > 1:   # a tie: the even code wins
+            codes = finite[np.isin(vals, best)]
+            assert inputs.f64_to_e4m3(np.array([xi]))[0] % 2 == 0 or ei == 0.0, (xi, codes)
+    assert inputs.f64_to_e4m3(np.array([1e6]))[0] == 0x7E
+    assert inputs.f64_to_e4m3(np.array([-1e6]))[0] == 0xFE
+
+
+def test_quantized_decode_cache_dequantises_within_half_a_step():
+    base = inputs.custom_decode(5, 8, 2, 128, 1, 200, seed=4)
+    f = inputs.quantize_decode_fp8(base)
+    for cache, qc, sc in ((base.k_cache, f.k_cache, f.k_scale), (base.v_cache, f.v_cache, f.v_scale)):
+        x = inputs.bf16_bits_to_f64(cache)
+        deq = inputs.e4m3_to_f64(qc) * sc[None, None, :, None]
+        # e4m3 has 3 mantissa bits: relative error <= 2^-4 for normal values, and
+        # absolute error <= half the subnormal step 2^-10 * scale below them
+        err = np.abs(deq - x)
+        bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * sc[None, None, :, None])
+        assert np.all(err <= bound * (1 + 1e-12))
+        assert np.abs(inputs.e4m3_to_f64(qc)).max() <= 448.0
