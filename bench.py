@@ -294,6 +294,24 @@ def main(argv=None):
             "ms_mean": round(t_ms, 4), "TFLOP/s": round(t_tf, 2),
             "frac_of_bf16_peak": round(t_tf / PEAK_BF16_TFLOPS, 4),
             "mfma_flops_executed_per_algorithmic": 1.5}
+        # Backward pass on the same workload: algorithmic flops 2.5x the forward's (dV,
+        # dP, dQ, dK and the recomputed S: 5 products of 2d flops per attending pair); the
+        # kernels execute 7 (S and dP are computed again for dQ).
+        log("[bench] extra: gqa_causal backward")
+        gdo = torch.randn(gq.shape, generator=torch.Generator(device=dev).manual_seed(5),
+                          device=dev).to(torch.bfloat16)
+        gdq, gdk, gdv = torch.empty_like(gq), torch.empty_like(gk), torch.empty_like(gv)
+        gws = torch.empty(_lib.fa_bwd_workspace_size(gcfg.B, gcfg.H, gcfg.Nq), dtype=torch.uint8,
+                          device=dev)
+        _lib.fa_fwd(gq, gk, gv, go, glse, causal=True, scale=gcfg.scale, stream=stream)
+        b_ms = timed(lambda: _lib.fa_bwd(gq, gk, gv, go, glse, gdo, gdq, gdk, gdv, causal=True,
+                                         scale=gcfg.scale, workspace=gws, stream=stream))
+        b_tf = 2.5 * gcfg.flops / (b_ms * 1e-3) / 1e12
+        out["legs"]["backward_gqa_causal"] = {
+            "ms_mean": round(b_ms, 4), "TFLOP/s": round(b_tf, 2),
+            "frac_of_bf16_peak": round(b_tf / PEAK_BF16_TFLOPS, 4),
+            "flops": 2.5 * gcfg.flops, "mfma_flops_executed_per_algorithmic": 1.4}
+        del gdo, gdq, gdk, gdv, gws
         del gq, gk, gv, go, glse
 
     if not args.no_extra:

@@ -64,6 +64,30 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            void* stream);
 
 /*
+ * fa_bwd — gradients of fa_fwd's output with respect to q, k and v, recomputing the
+ * attention probabilities from q, k and the forward's lse instead of storing them (page
+ * "Donanıma Duyarlı Algoritma Tasarımı: FlashAttention": only the per-row statistics of
+ * the forward stay in HBM; glossary entry "Flash Attention": intermediates are
+ * recomputed in the backward pass rather than saved). With P = exp(scale q k^T - lse)
+ * (masked entries 0) and D = rowsum(dO * O):
+ *   dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q,
+ * dK and dV summed over the query heads of each GQA group.
+ *   q, o, dout, dq  [B, H, Nq, d] bf16      k, v, dk, dv  [B, Hkv, Nk, d] bf16
+ *   lse             [B, H, Nq] fp32, the forward's (natural-log) lse for these q, k, v
+ *   workspace       device scratch of at least fa_bwd_workspace_size(B, H, Nq) bytes
+ * Same ranges and errors as fa_fwd; lse, dout, dq, dk, dv and workspace must be non-NULL
+ * and aligned (16 bytes; workspace 4), else FA_ERR_INVALID. dq, dk, dv are written (not
+ * accumulated into); gradients are accumulated in fp32 and rounded to bf16. Three
+ * kernels on the stream: D, then dK/dV, then dQ; deterministic (no atomics).
+ */
+size_t fa_bwd_workspace_size(int B, int H, int Nq);
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq,
+           int Nk, int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+           void* stream);
+
+/*
  * fa_fwd_two_pass — fa_fwd computed in the two passes of FlashAttention-1 (page
  * "Donanıma Duyarlı Algoritma Tasarımı: FlashAttention", section "FlashAttention-1
  * (İki Geçişli Yaklaşım)"): the first pass reads Q and K and writes only each row's

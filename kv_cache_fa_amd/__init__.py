@@ -9,6 +9,8 @@ call does, and raises if it has not been built.
 """
 from ._lib import (  # noqa: F401
     KvfaError,
+    fa_bwd,
+    fa_bwd_workspace_size,
     fa_decode_paged,
     fa_decode_paged_fp8,
     fa_decode_paged_split_tokens,

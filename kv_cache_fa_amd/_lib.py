@@ -33,6 +33,9 @@ SIGNATURES = {
     "fa_kv_append": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "fa_decode_paged_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i,
                                  _i, _i, _i, _f, _vp, _sz, _vp]),
+    "fa_bwd_workspace_size": (_sz, [_i, _i, _i]),
+    "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
+                    _vp, _sz, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
 }
 
@@ -273,4 +276,32 @@ def fa_decode_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, page_table, seq_l
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(page_table),
         _ptr(seq_lens), page_size, _ptr(o), _ptr(lse), S, H, Hkv, d, num_pages,
         int(page_table.shape[1]), int(max_seq_len), float(scale), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def fa_bwd_workspace_size(B, H, Nq) -> int:
+    return int(lib().fa_bwd_workspace_size(B, H, Nq))
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, *, causal: bool, scale: float, workspace,
+           stream=None):
+    """Backward pass. q,o,dout,dq [B,H,Nq,d] bf16; k,v,dk,dv [B,Hkv,Nk,d] bf16; lse
+    [B,H,Nq] fp32 from the forward; workspace: uint8 device tensor."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"),
+                 (dk, "dk"), (dv, "dv")):
+        _check_tensor(t, torch.bfloat16, n)
+    _check_tensor(lse, torch.float32, "lse")
+    B, H, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    _require(tuple(k.shape) == tuple(v.shape) == tuple(dk.shape) == tuple(dv.shape)
+             == (B, Hkv, Nk, d), "k/v/dk/dv shape mismatch")
+    _require(tuple(o.shape) == tuple(dout.shape) == tuple(dq.shape) == tuple(q.shape),
+             "o/dout/dq must have q's shape")
+    _require(tuple(lse.shape) == (B, H, Nq), "lse must be [B,H,Nq]")
+    _require(workspace.is_cuda and workspace.is_contiguous(), "workspace must be device memory")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("fa_bwd", lib().fa_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        B, H, Hkv, Nq, Nk, d, int(bool(causal)), float(scale), _ptr(workspace), ws_bytes,
         _stream(stream)))

@@ -199,6 +199,31 @@ int fa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_ca
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_bwd_workspace_size(int B, int H, int Nq) {
+    if (B < 1 || H < 1 || Nq < 1) return 0;
+    return kvfa::bwd_workspace_bytes(B, H, Nq);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq, int Nk,
+           int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+           void* stream) {
+    int st = check_prefill(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale, 2);
+    if (st != FA_OK) return st;
+    if (!lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_INVALID;
+    if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+        !aligned(workspace, 4))
+        return FA_ERR_INVALID;
+    if (workspace_bytes < kvfa::bwd_workspace_bytes(B, H, Nq)) return FA_ERR_INVALID;
+    const unsigned long long n_q = (unsigned long long)((Nq + 127) / 128) * B * H;
+    const unsigned long long n_k = (unsigned long long)((Nk + 127) / 128) * B * Hkv;
+    if (n_q >= (1ull << 31) || n_k >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+    hipError_t e = kvfa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, Nq, Nk, d,
+                                         causal != 0, scale, workspace,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
                         const float* k_scale, const float* v_scale,
                         const int32_t* page_table, const int32_t* seq_lens, int page_size,

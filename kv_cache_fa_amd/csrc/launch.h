@@ -37,6 +37,13 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache,
                             int n_new, int Hkv, int d, int num_pages, int max_pages_per_seq,
                             hipStream_t stream);
 
+// Backward pass: workspace bytes (the rows' D = rowsum(dO * O)) and the launcher.
+size_t bwd_workspace_bytes(int B, int H, int Nq);
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                           void* workspace, hipStream_t stream);
+
 // Decode split plan: tokens per split-K work-group, and the workspace it implies.
 int decode_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size);
 size_t decode_workspace_bytes(int num_seqs, int H, int Hkv, int d, int max_seq_len,

@@ -11,6 +11,7 @@ pure-Python brute force (``oracle.brute``). No function is "parity unpinned".
 from .attention import (  # noqa: F401
     allowed_keys,
     attention,
+    attention_backward,
     decode,
     gather_pages,
     merge_partials,

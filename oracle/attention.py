@@ -142,6 +142,41 @@ def attention(q, k, v, *, causal: bool, scale: float, rows=None, return_probs=Fa
     return (O, LSE, probs) if return_probs else (O, LSE)
 
 
+def attention_backward(q, k, v, do, *, causal: bool, scale: float, window=None):
+    """Gradients of O = softmax(scale Q K^T + mask) V, in float64 (dense).
+
+    The forward's definition (page "Donanıma Duyarlı Algoritma Tasarımı:
+    FlashAttention", section "Transformer Mimarisi ve Self-Attention Mekanizması")
+    differentiated by the chain rule, per (b, h), with P the probability matrix:
+    dV = P^T dO; dP = dO V^T; dS = P * (dP - rowsum(dP * P)) (softmax's Jacobian
+    applied row by row); dQ = scale dS K; dK = scale dS^T Q. Under GQA, dK and dV of a
+    K/V head sum over the query heads that read it. The forward keeps no P for this:
+    the backward recomputes it from Q, K and the rows' statistics (section
+    "FlashAttention'ın Temelleri", recomputation instead of storing intermediates).
+    Returns (dq [B,H,Nq,d], dk, dv [B,Hkv,Nk,d]).
+    """
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    B, H, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    g = H // Hkv
+    mask = window_mask(np.arange(Nq), Nq, Nk, causal, window)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            kvh = h // g
+            S = scale * (q[b, h] @ k[b, kvh].T)
+            P, _, _ = softmax_rows(S, mask)
+            dO = do[b, h]
+            dv[b, kvh] += P.T @ dO
+            dP = dO @ v[b, kvh].T
+            dS = P * (dP - np.sum(dP * P, axis=1, keepdims=True))
+            dq[b, h] = scale * (dS @ k[b, kvh])
+            dk[b, kvh] += scale * (dS.T @ q[b, h])
+    return dq, dk, dv
+
+
 def decode(q, k_seq, v_seq, *, scale: float):
     """Single-token decode against per-sequence cached K/V, in float64.
 

@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert set(declared_functions()) == {
         "fa_fwd", "fa_fwd_fp32", "fa_decode_paged", "fa_decode_paged_workspace_size",
-        "fa_decode_paged_split_tokens", "fa_fwd_paged", "fa_kv_append", "fa_fwd_window", "fa_fwd_two_pass", "fa_decode_paged_fp8", "fa_status_string"}
+        "fa_decode_paged_split_tokens", "fa_fwd_paged", "fa_kv_append", "fa_fwd_window", "fa_fwd_two_pass", "fa_decode_paged_fp8", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -169,6 +169,24 @@ def test_decode_fp8_validation(lib):
     assert call(S=0) == INVALID
     assert call(d=96) == UNSUPPORTED
     assert call(H=32, Hkv=5) == INVALID
+
+
+def test_bwd_validation(lib):
+    ws = lib.fa_bwd_workspace_size(1, 8, 64)
+    assert ws == 8 * 64 * 4
+    assert lib.fa_bwd_workspace_size(0, 8, 64) == 0
+
+    def call(**kw):
+        a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=8, Hkv=8, Nq=64,
+                 Nk=64, d=128, causal=1, scale=0.125, ws=P, ws_bytes=ws)
+        a.update(kw)
+        return lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                          a["dv"], a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                          a["causal"], a["scale"], a["ws"], a["ws_bytes"], None)
+    for kw in (dict(lse=None), dict(do=None), dict(dq=None), dict(dk=P + 8), dict(ws=None),
+               dict(ws_bytes=16), dict(Nq=65, Nk=64), dict(H=8, Hkv=3), dict(scale=0.0)):
+        assert call(**kw) == INVALID, kw
+    assert call(d=96) == UNSUPPORTED
 
 
 def test_workspace_size(lib):

@@ -180,6 +180,54 @@ def test_gather_pages_detects_a_wrong_slot():
     assert not np.array_equal(wrong, inp.k_seq[s])
 
 
+# ---- backward pass (analytic gradients, pinned by central differences) ------------
+def _loss(q, k, v, w, causal, scale, window=None):
+    O, _ = oracle.attention(q, k, v, causal=causal, scale=scale, window=window)
+    return float(np.sum(O * w))
+
+
+@pytest.mark.parametrize("causal,window,Hkv", [(False, None, 2), (True, None, 1),
+                                                (False, (1, 2), 2)])
+def test_backward_matches_central_differences(causal, window, Hkv):
+    """d(sum(O * W))/dX by central differences equals the analytic gradient with dO = W
+    (an independent check of every term: a dropped term, a sign or a transpose fails)."""
+    rng = np.random.default_rng(3)
+    B, H, Nq, Nk, d = 1, 2, 4, 5, 3
+    q = rng.standard_normal((B, H, Nq, d))
+    k = rng.standard_normal((B, Hkv, Nk, d))
+    v = rng.standard_normal((B, Hkv, Nk, d))
+    w = rng.standard_normal((B, H, Nq, d))
+    scale = 0.7
+    dq, dk, dv = oracle.attention_backward(q, k, v, w, causal=causal, scale=scale, window=window)
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            f1 = _loss(q, k, v, w, causal, scale, window)
+            x[idx] = old - eps
+            f0 = _loss(q, k, v, w, causal, scale, window)
+            x[idx] = old
+            num[idx] = (f1 - f0) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=0, atol=2e-8)
+
+
+def test_backward_closed_forms():
+    """Uniform attention (K = 0) over equal V rows: dV_j = sum_i dO_i / Nk and, since
+    every dP row is constant, dS = 0, so dQ = dK = 0."""
+    rng = np.random.default_rng(5)
+    Nq, Nk, d = 3, 4, 2
+    q = rng.standard_normal((1, 1, Nq, d))
+    k = np.zeros((1, 1, Nk, d))
+    v = np.tile(rng.standard_normal((1, 1, 1, d)), (1, 1, Nk, 1))
+    do = rng.standard_normal((1, 1, Nq, d))
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, causal=False, scale=0.5)
+    np.testing.assert_allclose(dv[0, 0], np.tile(do[0, 0].sum(0) / Nk, (Nk, 1)), atol=1e-15)
+    np.testing.assert_allclose(dq, 0.0, atol=1e-15)
+    np.testing.assert_allclose(dk, 0.0, atol=1e-15)
+
+
 # ---- FlashAttention-1 two passes ---------------------------------------------------
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_two_pass_equals_definition(seed):
