@@ -17,11 +17,14 @@
 // * dkdv_kernel: a work-group owns 128 keys of one (batch, KV head) (32 per wave, the
 //   wave's K and V rows held in registers) and sweeps every query tile of 32 rows of the
 //   g heads of its group, staged in LDS (Q, dO and the rows' lse and D, double-buffered,
-//   loaded straight from HBM). Per tile and wave: S = Q K^T and dP = dO V^T on
-//   v_mfma_f32_32x32x16_bf16 (Q / dO rows from LDS as A, K / V from registers as B), so
-//   each lane owns one key column; then dV^T += dO^T P and dK^T += Q^T dS with the
-//   transposed tiles read through ds_read_b64_tr_b16 and P, dS packed to bf16 from the
-//   score registers. Causal: query tiles wholly before the block's first key are skipped.
+//   loaded straight from HBM). Per tile and wave: S = Q K^T on v_mfma_f32_32x32x16_bf16
+//   (Q rows from LDS as A, K from registers as B), so each lane owns one key column;
+//   P = exp(scale S - lse); dV^T += dO^T P; dP = dO V^T; dS = P (dP - D); dK^T += Q^T dS
+//   (transposed tiles through ds_read_b64_tr_b16, P and dS packed to bf16 from the score
+//   registers) — in that order, so S/P and dP are never live together and two waves fit
+//   per SIMD. Causal: query tiles wholly before the block's first key are skipped.
+// * Q, dO and K tiles are read both as rows and transposed; their 16-byte chunks use the
+//   kt_swz swizzle, conflict-free for both patterns.
 // * dq_kernel: like the forward, a work-group owns 128 query rows (32 per wave, Q and dO
 //   rows in registers) and sweeps 64-key tiles of K and V in LDS: S^T = K Q^T,
 //   dP^T = V dO^T, dS^T = P^T * (dP^T - D), dQ^T += K^T dS^T (K^T through transposing
@@ -71,6 +74,10 @@ __device__ __forceinline__ void buf_load4_lds(__amdgpu_buffer_rsrc_t r, void* ld
 #endif
 }
 
+#ifndef DKDV_WAVES
+#define DKDV_WAVES 2
+#endif
+
 template <int D>
 struct BwdTile {
     static constexpr int ROW = D * 2;        // bytes per row
@@ -85,7 +92,7 @@ struct BwdTile {
     static_assert(QDMA >= 1 && KDMA >= 1, "whole 1 KiB loads per wave");
 };
 
-// Per-lane LDS offsets of a row-major tile with 16-byte chunks swizzled by k_swz:
+// Per-lane LDS offsets of a row-major tile with 16-byte chunks swizzled by kt_swz:
 // the A operand of a 32x32x16 MFMA read as rows (row = 32 kb + col, chunk 2s + g), and
 // the same tile read transposed (ds_read_b64_tr_b16; rows 16t + 4(G/2) + e and those
 // plus 8, chunk 4db + 2(G%2) + a/2, byte 8(a%2), G = lane/16, lane%16 = a + 4e).
@@ -98,20 +105,20 @@ struct TileReads {
         constexpr int ROW = D * 2;
         const int col = lane & 31, g = lane >> 5;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) row_off[s] = col * ROW + (((2 * s + g) ^ k_swz<D>(col)) * 16);
+        for (int s = 0; s < D / 16; ++s) row_off[s] = col * ROW + (((2 * s + g) ^ kt_swz<D>(col)) * 16);
         const int vG = lane >> 4, va = lane & 3, ve = (lane >> 2) & 3;
         const int vrow = (vG >> 1) * 4 + ve;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
             const int lc = 4 * db + 2 * (vG & 1) + (va >> 1);
-            tr_off0[db] = vrow * ROW + ((lc ^ k_swz<D>(vrow)) * 16) + 8 * (va & 1);
-            tr_off1[db] = (vrow + 8) * ROW + ((lc ^ k_swz<D>(vrow + 8)) * 16) + 8 * (va & 1);
+            tr_off0[db] = vrow * ROW + ((lc ^ kt_swz<D>(vrow)) * 16) + 8 * (va & 1);
+            tr_off1[db] = (vrow + 8) * ROW + ((lc ^ kt_swz<D>(vrow + 8)) * 16) + 8 * (va & 1);
         }
     }
 };
 
 // Direct-load offsets: piece i of wave w covers tile bytes [1024 (NP w + i), +1024); lane L
-// fills byte 16 L of it: row r, physical chunk pc <- logical chunk pc ^ k_swz(r) of row r.
+// fills byte 16 L of it: row r, physical chunk pc <- logical chunk pc ^ kt_swz(r) of row r.
 template <int D, int NP>
 __device__ __forceinline__ void dma_offsets(int w, int lane, uint32_t (&off)[NP]) {
     constexpr int ROW = D * 2;
@@ -119,7 +126,7 @@ __device__ __forceinline__ void dma_offsets(int w, int lane, uint32_t (&off)[NP]
     for (int i = 0; i < NP; ++i) {
         const int byte = 1024 * (NP * w + i) + 16 * lane;
         const int r = byte / ROW, pc = (byte % ROW) / 16;
-        off[i] = (uint32_t)(r * ROW + ((pc ^ k_swz<D>(r)) * 16));
+        off[i] = (uint32_t)(r * ROW + ((pc ^ kt_swz<D>(r)) * 16));
     }
 }
 
@@ -133,7 +140,7 @@ __device__ __forceinline__ u32x4 tr_operand(const char* base, int off0, int off1
 
 // ---- dK, dV ------------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DKDV_WAVES, DKDV_WAVES)))
 void dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                  const float* __restrict__ lse, const float* __restrict__ delta,
@@ -150,8 +157,11 @@ void dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, g = lane >> 5;
-    const int kb = blockIdx.x % n_kb;
-    const int bk = blockIdx.x / n_kb;  // b * Hkv + kvh
+    // Key blocks vary slowest: under causal masking block kb sees the most query tiles
+    // when kb is small, so the longest work-groups are dispatched first.
+    const int n_bk = gridDim.x / n_kb;
+    const int kb = blockIdx.x / n_bk;
+    const int bk = blockIdx.x % n_bk;  // b * Hkv + kvh
     const int b = bk / Hkv, kvh = bk % Hkv;
     const int gq = H / Hkv;
     const int k0 = kb * 128;
@@ -208,48 +218,64 @@ void dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     auto tile = [&](int t, const char* qst, const char* dst, const float (*sst)[64]) {
         const int qt = qt0 + t % per_head;
         const int q0 = qt * T::BQ;
-        // S[q][key] and dP[q][key]: lane holds rows q = 8(i/4) + 4g + i%4 of its key column.
-        f32x16 sa = f32x16{}, pa = f32x16{};
+        // S[q][key]: lane holds rows q = 8(i/4) + 4g + i%4 of its key column.
+        f32x16 sa = f32x16{};
 #pragma unroll
         for (int s = 0; s < T::KS; ++s) {
             const u32x4 aq = *reinterpret_cast<const u32x4*>(qst + rd.row_off[s]);
-            const u32x4 ad = *reinterpret_cast<const u32x4*>(dst + rd.row_off[s]);
             sa = mfma32x32x16(aq, kf[s], sa);
-            pa = mfma32x32x16(ad, vf[s], pa);
         }
-        // P = exp(scale s - lse), dS = P (dP - D); zero outside the mask and past Nq.
-        u32x4 pp[2], ps[2];
+        // P = exp(scale s - lse), zero outside the mask and past Nq; packed for the
+        // 16-query steps (rows 16t' + 4g + {0..3}, then 16t' + 8 + 4g + {0..3}).
+        u32x4 pp[2];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {  // row group r: rows 8r + 4g + 0..3
             const int rl = 8 * r + 4 * g;
             const f32x4 lv = *reinterpret_cast<const f32x4*>(&sst[0][rl]);
-            const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&sst[1][rl]);
-            float pv[4], sv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int qa = q0 + rl + e;
                 bool ok = qa < Nq;
                 if (CAUSAL) ok = ok && key <= qa + off;
-                const float p = ok ? fast_exp2(fmaf(sa[4 * r + e], scale_log2, -lv[e] * kLog2e)) : 0.f;
-                pv[e] = p;
-                sv[e] = p * (pa[4 * r + e] - dv4[e]);
+                sa[4 * r + e] = ok ? fast_exp2(fmaf(sa[4 * r + e], scale_log2, -lv[e] * kLog2e)) : 0.f;
             }
-            // B operand of step t' = r / 2 takes rows 16t' + 4g + {0..3} (r even) and
-            // 16t' + 8 + 4g + {0..3} (r odd), in that order.
             const int tt = r >> 1, half = (r & 1) * 2;
-            pp[tt][half] = pack_bf16x2(pv[0], pv[1]);
-            pp[tt][half + 1] = pack_bf16x2(pv[2], pv[3]);
-            ps[tt][half] = pack_bf16x2(sv[0], sv[1]);
-            ps[tt][half + 1] = pack_bf16x2(sv[2], sv[3]);
+            pp[tt][half] = pack_bf16x2(sa[4 * r], sa[4 * r + 1]);
+            pp[tt][half + 1] = pack_bf16x2(sa[4 * r + 2], sa[4 * r + 3]);
         }
-        // dV^T += dO^T P, dK^T += Q^T dS (transposed tiles through transposing reads).
+        // dV^T += dO^T P (dO^T through transposing reads).
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int db = 0; db < T::DB; ++db) {
                 const u32x4 ado = tr_operand(dst + tt * 16 * T::ROW, rd.tr_off0[db], rd.tr_off1[db]);
-                const u32x4 aq = tr_operand(qst + tt * 16 * T::ROW, rd.tr_off0[db], rd.tr_off1[db]);
                 dva[db] = mfma32x32x16(ado, pp[tt], dva[db]);
+            }
+        // dP[q][key] = dO V^T, then dS = P (dP - D), packed like P.
+        f32x16 pa = f32x16{};
+#pragma unroll
+        for (int s = 0; s < T::KS; ++s) {
+            const u32x4 ad = *reinterpret_cast<const u32x4*>(dst + rd.row_off[s]);
+            pa = mfma32x32x16(ad, vf[s], pa);
+        }
+        u32x4 ps[2];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rl = 8 * r + 4 * g;
+            const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&sst[1][rl]);
+            float sv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[e] = sa[4 * r + e] * (pa[4 * r + e] - dv4[e]);
+            const int tt = r >> 1, half = (r & 1) * 2;
+            ps[tt][half] = pack_bf16x2(sv[0], sv[1]);
+            ps[tt][half + 1] = pack_bf16x2(sv[2], sv[3]);
+        }
+        // dK^T += Q^T dS (Q^T through transposing reads).
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db) {
+                const u32x4 aq = tr_operand(qst + tt * 16 * T::ROW, rd.tr_off0[db], rd.tr_off1[db]);
                 dka[db] = mfma32x32x16(aq, ps[tt], dka[db]);
             }
     };

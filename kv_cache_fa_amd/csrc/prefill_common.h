@@ -23,6 +23,17 @@ __device__ __forceinline__ int v_swz(int row) {
     else return 4 * ((row >> 1) & 1);
 }
 
+// Swizzle for a tile read both ways: as rows (16 consecutive rows, one chunk) and through
+// transposing reads (4 consecutive rows, an aligned group of 4 chunks). For D = 128 the
+// row's low two bits pick the group of 4 chunks and bits 2-3 the chunk inside it, so 16
+// consecutive rows hit 16 different chunks and 4 consecutive rows 4 different groups.
+// For D = 64 two rows share a 256-byte bank cycle, so the same holds per row parity.
+template <int D>
+__device__ __forceinline__ int kt_swz(int row) {
+    if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);
+    else return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+}
+
 // Work-group id -> (batch*H + head, q tile). The dispatcher places work-group i on XCD
 // i % 8, and each XCD has its own L2. When the (batch, head) count is a multiple of 8,
 // XCD x owns a contiguous block of (batch, head) pairs; if that block holds whole GQA
