@@ -15,7 +15,11 @@
 //   served from one read of each K/V page, so every cached byte is read once.
 // * Scores: S^T[token][head] = K_page Q^T with v_mfma_f32_16x16x32_bf16 — one page
 //   (16 tokens) is exactly the MFMA's 16 rows, the group's heads fill its columns.
-//   K rows go straight from HBM into the A operand (no LDS).
+//   The MFMA wants one token per lane of a 16-lane group, HBM wants whole rows per
+//   16 lanes: K pages therefore go HBM -> LDS by direct loads (buffer_load ... lds, each
+//   instruction 1 KiB of whole rows, 16-byte chunks XOR-swizzled by row) into a
+//   per-wave double buffer, and the A operand is read from there without bank
+//   conflicts.
 // * P.V: plain FMAs. A lane owns one 16-byte chunk of V rows (8 dims) for a subset of
 //   the page's tokens and accumulates all heads of the group; the probabilities reach
 //   it through a small per-wave LDS table.
@@ -52,11 +56,26 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     constexpr int TG = 64 / CH;        // token groups of the P.V lane layout
     constexpr int TPL = kPage / TG;    // tokens per lane in P.V
     constexpr int KS = D / 32;         // MFMA k-steps over the head dimension
+    constexpr int ROWB = D * ES;       // bytes of one cached row (token, KV head)
+    constexpr int KCH = ROWB / 16;     // 16-byte chunks per row
+    constexpr int PAGEB = kPage * ROWB;            // bytes of one page's K rows
+    constexpr int KDMA = PAGEB / 1024;             // 1 KiB direct loads per page
+    static_assert(KDMA >= 1 && KDMA * 1024 == PAGEB, "whole 1 KiB loads per page");
+    // Per wave: two K stages (separate arrays, so the compiler can tell a read of one from
+    // the direct loads into the other); after the wave's loop its partial output for the
+    // cross-wave merge reuses the first stage when it fits.
+    __shared__ __attribute__((aligned(1024))) char kst_a[kWaves][PAGEB];
+    __shared__ __attribute__((aligned(1024))) char kst_b[kWaves][PAGEB];
+    constexpr bool RO_IN_A = GH * D * 4 <= PAGEB;
+    __shared__ float red_o_x[RO_IN_A ? 1 : kWaves * GH * D];
+    auto red_o = [&](int ww) -> float* {  // [GH][D] of wave ww
+        if constexpr (RO_IN_A) return reinterpret_cast<float*>(kst_a[ww]);
+        else return red_o_x + ww * GH * D;
+    };
     __shared__ float p_lds[kWaves][kPage][GH];
     __shared__ float a_lds[kWaves][GH];
     __shared__ float red_m[kWaves][GH];
     __shared__ float red_l[kWaves][GH];
-    __shared__ float red_o[kWaves][GH][D];
 
     const int s = blockIdx.z;
     const int kvh = blockIdx.x / n_hg, hg = blockIdx.x % n_hg;
@@ -118,32 +137,59 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     // makes them return zeros without touching memory), so the wait counts stay exact.
     // The cache is read once per call: the loads carry the nontemporal hint.
     const uint32_t span = (uint32_t)((kPage - 1) * tok_stride + D) * ES;
-    const uint32_t k_off = (uint32_t)(n * tok_stride + kq * 8) * ES;
     const uint32_t v_off = (uint32_t)(tg * tok_stride + c * 8) * ES;
+    // K direct loads: lane L of the i-th 1 KiB piece fills stage byte 1024 i + 16 L, i.e.
+    // row r, physical chunk pc, with logical chunk pc ^ (r % KCH) of cached row r.
+    uint32_t kd_off[KDMA];
+#pragma unroll
+    for (int i = 0; i < KDMA; ++i) {
+        const int byte = 1024 * i + 16 * lane;
+        const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+        kd_off[i] = (uint32_t)(r * tok_stride * ES + ((pc ^ (r % KCH)) * 16));
+    }
+    // A operand of k-step j: token n, elements 32 j + 8 kq .. +7 (8 ES bytes).
+    int kr_off[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+        const int b = (32 * j + 8 * kq) * ES;
+        kr_off[j] = n * ROWB + (((b / 16) ^ (n % KCH)) * 16) + b % 16;
+    }
+    char* const kst0 = kst_a[w];
+    char* const kst1 = kst_b[w];
     auto load8 = [&](__amdgpu_buffer_rsrc_t r, uint32_t off) -> KVec {
         if constexpr (FP8) return buf_load8_nt(r, off);
         else return buf_load16_nt(r, off);
     };
-    auto load_page = [&](int it, KVec (&kf)[KS], KVec (&vv)[TPL]) -> bool {
+    auto load_page = [&](int it, char* kst, KVec (&vv)[TPL]) -> bool {
         const int pid = __builtin_amdgcn_readlane(pid_lane, it);
         const bool valid = (unsigned)pid < (unsigned)num_pages;
         const size_t page_base = (size_t)(valid ? pid : 0) * kPage * tok_stride + (size_t)kvh * D;
         const auto rk = make_rsrc(static_cast<const char*>(kcache) + page_base * ES, valid ? span : 0u);
         const auto rv = make_rsrc(static_cast<const char*>(vcache) + page_base * ES, valid ? span : 0u);
 #pragma unroll
-        for (int j = 0; j < KS; ++j) kf[j] = load8(rk, k_off + j * 32 * ES);
+        for (int i = 0; i < KDMA; ++i) buf_load16_lds(rk, kst + 1024 * i, kd_off[i], 0u);
 #pragma unroll
         for (int i = 0; i < TPL; ++i)
             vv[i] = load8(rv, v_off + (uint32_t)(TG * i * tok_stride) * ES);
         return valid;
     };
 
-    KVec kA[KS], vA[TPL], kB[KS], vB[TPL];
-    bool okA = load_page(0, kA, vA);   // a lane past the wave's pages holds id -1
+    KVec vA[TPL], vB[TPL];
+    bool okA = load_page(0, kst0, vA);   // a lane past the wave's pages holds id -1
     bool okB = false;
-    auto page_compute = [&](const KVec (&KF)[KS], const KVec (&VV)[TPL], const bool OK, const int IT) {
+    // Every load of the page before this one's successor has landed: its K rows in LDS
+    // (direct loads are counted by vmcnt only) and its V registers.
+    auto wait_page = [&]() __attribute__((always_inline)) {
+        constexpr int later = KDMA + TPL;  // loads of the page issued after it
+        static_assert(later < 64, "vmcnt field");
+        __builtin_amdgcn_s_waitcnt((later & 15) | ((later >> 4) << 14) | (7 << 4) | (15 << 8));
+    };
+    auto page_compute = [&](const char* KST, const KVec (&VV)[TPL], const bool OK, const int IT) {
         if (OK) {
             const int tok0 = (first_page + w + kWaves * IT) * kPage;
+            KVec KF[KS];
+#pragma unroll
+            for (int j = 0; j < KS; ++j) KF[j] = *reinterpret_cast<const KVec*>(KST + kr_off[j]);
 
             // S^T: acc[i] = score of token 4*kq + i for head column n
             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -217,11 +263,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         }
     };
     for (int it = 0; it < n_my; it += 2) {
-        okB = load_page(it + 1, kB, vB);
-        page_compute(kA, vA, okA, it);
-        okA = load_page(it + 2, kA, vA);
-        page_compute(kB, vB, okB, it + 1);
+        okB = load_page(it + 1, kst1, vB);
+        wait_page();
+        page_compute(kst0, vA, okA, it);
+        okA = load_page(it + 2, kst0, vA);
+        wait_page();
+        page_compute(kst1, vB, okB, it + 1);
     }
+    // The loop ends with two pages' loads still in flight (past the wave's last page: zero
+    // descriptors, but their LDS writes land in the stages reused below).
+    __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));
 
     // ---- reduce within the wave, then across the 4 waves ----
     float l = l_part;
@@ -241,10 +292,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         red_l[w][n] = l;
     }
     if (tg == 0) {
+        float* ro = red_o(w);
 #pragma unroll
         for (int hh = 0; hh < GH; ++hh)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) red_o[w][hh][c * 8 + e] = oacc[hh][e];
+            for (int e = 0; e < 8; ++e) ro[hh * D + c * 8 + e] = oacc[hh][e];
     }
     __syncthreads();
 
@@ -260,7 +312,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
                 const float mw = red_m[ww][hh];  // -inf for a wave that saw no token
                 const float f = mw == -INFINITY ? 0.f : fast_exp2((mw - M) * scale_log2);
                 lsum = fmaf(f, red_l[ww][hh], lsum);
-                acc = fmaf(f, red_o[ww][hh][dd], acc);
+                acc = fmaf(f, red_o(ww)[hh * D + dd], acc);
             }
         }
         const size_t row = ((size_t)s * H + h0 + hh) * max_splits + split;
@@ -271,57 +323,88 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 }
 
 // Merge the splits of each (sequence, head): LSE = log2 sum_k 2^lse_k (relative to the
-// largest), O = sum_k 2^(lse_k - LSE) O_k. A work-group of 256 threads takes one
-// sequence and kCombineHeads consecutive heads; a head's D outputs are spread over
-// D / kCombinePer threads, so every split's partial row is read with consecutive lanes.
+// largest), O = sum_k 2^(lse_k - LSE) O_k. One wave per (sequence, head), kCombineHeads
+// heads per work-group. The split statistics are spread over the lanes (one split per
+// lane, wave reductions for the max and the sum); each lane then owns D/64 output dims and
+// walks the splits with eight partial rows in flight, the weights broadcast from the lane
+// that holds them.
 constexpr int kCombineHeads = 4;
 template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(
+__global__ __launch_bounds__(64 * kCombineHeads) void decode_combine_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part,
     const int32_t* __restrict__ seq_lens, uint16_t* __restrict__ o, float* __restrict__ lse,
     int H, int max_seq_len, int split_tokens, int max_splits) {
-    constexpr int TPH = 256 / kCombineHeads;  // threads per head
-    constexpr int PER = D / TPH;              // output dims per thread (2 or 1)
-    const int s = blockIdx.y, tid = threadIdx.x;
-    const int h = blockIdx.x * kCombineHeads + tid / TPH;
-    const int lt = tid % TPH;
-    if (h >= H) return;
+    constexpr int PER = D / 64;  // output dims per lane (2 or 1)
+    const int s = blockIdx.y, lane = threadIdx.x & 63;
+    const int h = blockIdx.x * kCombineHeads + (threadIdx.x >> 6);
+    if (h >= H) return;  // uniform per wave
     const int L = min(max(seq_lens[s], 0), max_seq_len);
     const int ns = (L + split_tokens - 1) / split_tokens;
     const size_t row = (size_t)s * H + h;
     const float* lp = lse_part + row * max_splits;
+    const float* op = o_part + row * max_splits * D + lane * PER;
 
-    float M = -INFINITY;
-    for (int kk = 0; kk < ns; ++kk) M = fmaxf(M, lp[kk]);
+    float m = -INFINITY;
+    for (int k = lane; k < ns; k += 64) m = fmaxf(m, lp[k]);
+#pragma unroll
+    for (int msk = 1; msk < 64; msk <<= 1) m = fmaxf(m, shfl_xor(m, msk));
+    const float M = m;  // -inf: no split holds a token (L = 0)
+
     float out[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) out[e] = 0.f;
-    float W = 0.f;
+    float wsum = 0.f;
     if (M != -INFINITY) {
-        for (int kk = 0; kk < ns; ++kk) {
-            const float f = fast_exp2(lp[kk] - M);
-            W += f;
-            const float* op = o_part + (row * max_splits + kk) * D + lt * PER;
-            if constexpr (PER == 2) {
-                const f32x2 x = *reinterpret_cast<const f32x2*>(op);
-                out[0] = fmaf(f, x[0], out[0]);
-                out[1] = fmaf(f, x[1], out[1]);
-            } else {
-                out[0] = fmaf(f, op[0], out[0]);
+        for (int kb = 0; kb < ns; kb += 64) {
+            // weight of split kb + lane (0 past the last split)
+            const float fl = kb + lane < ns ? fast_exp2(lp[kb + lane] - M) : 0.f;
+            wsum += fl;
+            const int cnt = min(64, ns - kb);
+            auto fw = [&](int kk) {
+                return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl), kk));
+            };
+            int kk = 0;
+            for (; kk + 8 <= cnt; kk += 8) {
+                float x[8][PER];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float* src = op + (size_t)(kb + kk + u) * D;
+                    if constexpr (PER == 2) {
+                        const f32x2 v2 = *reinterpret_cast<const f32x2*>(src);
+                        x[u][0] = v2[0];
+                        x[u][1] = v2[1];
+                    } else {
+                        x[u][0] = src[0];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float f = fw(kk + u);
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) out[e] = fmaf(f, x[u][e], out[e]);
+                }
+            }
+            for (; kk < cnt; ++kk) {
+                const float f = fw(kk);
+                const float* src = op + (size_t)(kb + kk) * D;
+#pragma unroll
+                for (int e = 0; e < PER; ++e) out[e] = fmaf(f, src[e], out[e]);
             }
         }
-        const float inv = 1.f / W;
+#pragma unroll
+        for (int msk = 1; msk < 64; msk <<= 1) wsum += shfl_xor(wsum, msk);
+        const float inv = 1.f / wsum;
 #pragma unroll
         for (int e = 0; e < PER; ++e) out[e] *= inv;
     }
-    uint16_t* orow = o + row * D + lt * PER;
+    uint16_t* orow = o + row * D + lane * PER;
     if constexpr (PER == 2) {
         *reinterpret_cast<uint32_t*>(orow) = pack_bf16x2(out[0], out[1]);
     } else {
         orow[0] = (uint16_t)(pack_bf16x2(out[0], 0.f) & 0xffffu);
     }
-    if (lse != nullptr && lt == 0)
-        lse[row] = M != -INFINITY ? (M + fast_log2(W)) * kLn2 : -INFINITY;
+    if (lse != nullptr && lane == 0)
+        lse[row] = M != -INFINITY ? (M + fast_log2(wsum)) * kLn2 : -INFINITY;
 }
 
 template <int D, int GH, bool FP8>
@@ -419,13 +502,13 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
     if (e != hipSuccess) return e;
     dim3 grid((H + kCombineHeads - 1) / kCombineHeads, num_seqs);
     if (d == 128)
-        hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(256), 0, stream, o_part,
-                           lse_part, seq_lens, static_cast<uint16_t*>(o), lse, H, max_seq_len, T,
-                           max_splits);
+        hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(64 * kCombineHeads), 0, stream,
+                           o_part, lse_part, seq_lens, static_cast<uint16_t*>(o), lse, H,
+                           max_seq_len, T, max_splits);
     else
-        hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(256), 0, stream, o_part,
-                           lse_part, seq_lens, static_cast<uint16_t*>(o), lse, H, max_seq_len, T,
-                           max_splits);
+        hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(64 * kCombineHeads), 0, stream,
+                           o_part, lse_part, seq_lens, static_cast<uint16_t*>(o), lse, H,
+                           max_seq_len, T, max_splits);
     return hipGetLastError();
 }
 
