@@ -76,6 +76,15 @@ __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* l
 #endif
 }
 
+// The same with the nontemporal hint, for data read once per call.
+__device__ __forceinline__ void buf_load16_lds_nt(__amdgpu_buffer_rsrc_t r, void* lds_base,
+                                                  uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff, 0, 2);
+#endif
+}
+
 // ---- bf16 <-> fp32 --------------------------------------------------------------
 // Low / high bf16 of a packed dword, widened exactly.
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         const auto rk = make_rsrc(static_cast<const char*>(kcache) + page_base * ES, valid ? span : 0u);
         const auto rv = make_rsrc(static_cast<const char*>(vcache) + page_base * ES, valid ? span : 0u);
 #pragma unroll
-        for (int i = 0; i < KDMA; ++i) buf_load16_lds(rk, kst + 1024 * i, kd_off[i], 0u);
+        for (int i = 0; i < KDMA; ++i) buf_load16_lds_nt(rk, kst + 1024 * i, kd_off[i], 0u);
 #pragma unroll
         for (int i = 0; i < TPL; ++i)
             vv[i] = load8(rv, v_off + (uint32_t)(TG * i * tok_stride) * ES);
