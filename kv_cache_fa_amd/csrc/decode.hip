@@ -447,12 +447,18 @@ hipError_t launch_split_d(int GH, const void* q, const void* kc, const void* vc,
 }  // namespace
 
 int decode_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size) {
-    // Long splits keep the partial-result traffic small (one fp32 row of d per head
-    // and split); shorter ones are used when too few work-groups would be launched.
-    // (T <= 512 keeps every wave's page count, plus the two pages it prefetches past its
-    // last one, within the 64 lanes that hold its page ids.)
+    // A work-group has a fixed cost (page ids, first loads, merging its waves, writing
+    // its partial result) and the last round of work-groups leaves CUs idle. Splits of 512
+    // tokens are lengthened (in steps of 128) while the launch would exceed about six
+    // rounds of resident work-groups (256 CUs x 4), and shortened when fewer than 2048
+    // work-groups would be launched. (T <= 2048 keeps every wave's page count, plus the
+    // two pages it prefetches past its last one, within the 64 lanes that hold its page
+    // ids.)
+    constexpr long long kResident = 256 * 4;
+    auto wgs = [&](int T) { return (long long)num_seqs * Hkv * ((max_seq_len + T - 1) / T); };
     int T = 512;
-    while (T > 64 && (long long)num_seqs * Hkv * ((max_seq_len + T - 1) / T) < 2048) T >>= 1;
+    while (T < 2048 && wgs(T) > 6 * kResident) T += 128;
+    while (T > 64 && wgs(T) < 2048) T >>= 1;
     if (T < page_size) T = page_size;
     return T;
 }

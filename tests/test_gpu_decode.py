@@ -59,6 +59,16 @@ def test_decode_shapes(S, H, Hkv, d, lo, hi):
     _check(inp, f"decode S{S} H{H} Hkv{Hkv} d{d}")
 
 
+def test_decode_long_splits():
+    """A large max_seq_len grows the split to its 2048-token maximum (32 pages per wave
+    plus the two prefetched past the end, all within the page-id lanes); the actual
+    lengths cover one to two splits."""
+    from kv_cache_fa_amd import _lib
+    assert _lib.fa_decode_paged_split_tokens(48, 8, 32768, 16) == 2048
+    inp = inputs.custom_decode(48, 8, 8, 64, 1, 4096, max_seq_len=32768, seed=321)
+    _check(inp, "decode long splits")
+
+
 def test_decode_edge_lengths():
     """Empty sequence, one token, page boundaries (15, 16, 17), split boundaries."""
     cfg = inputs.DecodeConfig("edges", 10, 8, 2, 128, 0, 0, 16, 1100, 1 / math.sqrt(128), 3)
