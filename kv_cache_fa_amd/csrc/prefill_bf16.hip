@@ -1,7 +1,8 @@
 // bf16 exact attention (prefill) on gfx950 MFMA, fp32 accumulation: the four-wave kernel
-// behind chunked prefill through the page table (fa_fwd_paged) and sliding-window
-// prefill (fa_fwd_window). Contiguous full / causal prefill (fa_fwd) runs the ping-pong
-// kernel of prefill_pp.hip, which does the same arithmetic in the same order.
+// behind chunked prefill through the page table (fa_fwd_paged) and the two-pass form
+// (fa_fwd_two_pass). Contiguous full / causal and sliding-window prefill (fa_fwd,
+// fa_fwd_window) run the ping-pong kernel of prefill_pp.hip, which does the same
+// arithmetic in the same order.
 //
 // Method (page "Donanıma Duyarlı Algoritma Tasarımı: FlashAttention"):
 // * K and V are split into tiles that are staged in LDS, the CU's fast on-chip
@@ -91,29 +92,18 @@ struct PagedKV {
     int max_pages, num_pages, max_seq_len;
 };
 
-// Sliding window (WINDOW = true; glossary entry "Kayan Pencere Dikkati (Sliding Window
-// Attention)": a token attends only the keys within a fixed distance of its own
-// position). Query i at position p = Nk - Nq + i attends keys p - left .. p + right;
-// an unbounded side is passed as kUnbounded. Only the key tiles that intersect some row's
-// window are visited, each with the masked body. A row's first visited tile may hold
-// none of its keys, so its running max can still be -inf.
-constexpr int kUnbounded = 1 << 29;
-struct Window {
-    int left, right;
-};
-
 // Two passes (PASS = 1, then PASS = 2; page "Donanıma Duyarlı Algoritma Tasarımı:
 // FlashAttention", section "FlashAttention-1 (İki Geçişli Yaklaşım)"): the first pass
 // sweeps K only and keeps each row's running max and sum, leaving the row statistics in
 // HBM as lse = M + ln L; the second recomputes the scores, normalises them directly with
 // those statistics (P = exp(scale s - lse)) and accumulates P V, with no rescaling.
 // PASS = 0 is the usual single pass.
-template <int D, bool CAUSAL, bool PAGED, bool WINDOW, int PASS = 0>
+template <int D, bool CAUSAL, bool PAGED, int PASS = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                      float* __restrict__ lse, int H, int Hkv, int Nq, int Nk_arg, int n_qt,
-                     int BH, float scale_log2, float tau_raw, PagedKV pg, Window win) {
+                     int BH, float scale_log2, float tau_raw, PagedKV pg) {
     using T = Tile<D>;
     constexpr int BN = T::BN;
     __shared__ __attribute__((aligned(1024))) char ks0[T::TILE];
@@ -185,13 +175,6 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         const int last_row = min(q0 + T::BM, Nq) - 1;
         n_tiles = min(n_all, (last_row + off) / BN + 1);
         full = min(full, (q0 + off + 1) / BN);
-    }
-    // Tiles j_begin .. j_end-1 are visited (a band of tiles for a sliding window).
-    int j_begin = 0, j_end = n_tiles;
-    if constexpr (WINDOW) {
-        const int last_row = min(q0 + T::BM, Nq) - 1;
-        j_begin = max(0, q0 + off - win.left) / BN;
-        j_end = min(Nk - 1, last_row + off + win.right) / BN + 1;
     }
 
     // Direct loads: the wave's i-th 1 KiB piece of a tile covers tile bytes
@@ -319,23 +302,14 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             // it is dead past the row's last key and past Nk.
             int lim = Nk - 1 - j * BN - 4 * g;
             if (CAUSAL) lim = min(lim, qrow + off - j * BN - 4 * g);
-            int lo = -kUnbounded;  // keys before the row's window are dead too
-            if (WINDOW) {
-                lim = min(lim, qrow + off + win.right - j * BN - 4 * g);
-                lo = qrow + off - win.left - j * BN - 4 * g;
-            }
 #pragma unroll
             for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = kb * 32 + (i >> 2) * 8 + (i & 3);
-                    if (key > lim || (WINDOW && key < lo)) sacc[kb][i] = -INFINITY;
-                }
+                for (int i = 0; i < 16; ++i)
+                    if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sacc[kb][i] = -INFINITY;
         }
-        // Without a window every row attends key 0 (causal rows see the whole prefix),
-        // so after the first tile the max is finite and no -inf - -inf can occur; with a
-        // window the reference stays -inf until the row's first key and is then moved
-        // (alpha = 0 clears nothing but zeros).
+        // Every row attends key 0 (causal rows see the whole prefix), so after the first
+        // tile the max is finite and no -inf - -inf can occur.
         if constexpr (PASS != 2) {
         float mx = sacc[0][0];
 #pragma unroll
@@ -362,8 +336,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             }
         }
         }
-        const float mb = PASS == 2 ? mb_fixed
-                                   : (WINDOW && m_used == -INFINITY) ? 0.f : m_used * scale_log2;
+        const float mb = PASS == 2 ? mb_fixed : m_used * scale_log2;
 #pragma unroll
         for (int t = 0; t < T::PS; ++t) {
             const int kb = t >> 1, base = (t & 1) * 8;
@@ -408,13 +381,13 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         char* k_nxt = pv ? ks0 : ks1;   // K_{j+1}
         char* v_cur = pv ? vs1 : vs0;   // V_j
         char* v_nxt = pv ? vs0 : vs1;   // receives V_{j+1}
-        if (j + 2 < j_end) load_k(j + 2, k_cur);
-        if (PASS != 1 && j + 1 < j_end) load_v(j + 1, v_nxt);
+        if (j + 2 < n_tiles) load_k(j + 2, k_cur);
+        if (PASS != 1 && j + 1 < n_tiles) load_v(j + 1, v_nxt);
         if constexpr (PAGED) {  // page ids for the next step's loads
             pid_v = pid_k;
             pid_k = page_of(j + 3);
         }
-        if (j + 1 < j_end) scores(k_nxt, Next{});
+        if (j + 1 < n_tiles) scores(k_nxt, Next{});
         softmax_pv(j, v_cur, par, masked);
         __syncthreads();  // completes the loads above and publishes K_{j+2}, V_{j+1}
     };
@@ -433,33 +406,24 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         pid_k = pk_save;
         pid_v = pv_save;
     } else {
-        load_k(j_begin, ks0);
-        if (PASS != 1) load_v(j_begin, vs0);
-        if (j_begin + 1 < j_end) load_k(j_begin + 1, ks1);
+        load_k(0, ks0);
+        if (PASS != 1) load_v(0, vs0);
+        if (n_tiles > 1) load_k(1, ks1);
     }
     __syncthreads();
     scores(ks0, P0{});
     __syncthreads();
 
-    if constexpr (WINDOW) {
-        // Every tile runs the masked body: one body keeps the loop within the register
-        // budget, and the window's edges cut most tiles when the window is narrow.
-        for (int j = j_begin; j < j_end; j += 2) {
-            step(j, P0{}, std::true_type{});
-            if (j + 1 < j_end) step(j + 1, P1{}, std::true_type{});
-        }
-    } else {
-        // Unmasked tiles two at a time (stage parity alternates), then the rest with masking.
-        const int n_plain = min(full, n_tiles);
-        int j = 0;
-        for (; j + 1 < n_plain; j += 2) {
-            step(j, P0{}, std::false_type{});
-            step(j + 1, P1{}, std::false_type{});
-        }
-        for (; j < n_tiles; j += 2) {
-            step(j, P0{}, std::true_type{});
-            if (j + 1 < n_tiles) step(j + 1, P1{}, std::true_type{});
-        }
+    // Unmasked tiles two at a time (stage parity alternates), then the rest with masking.
+    const int n_plain = min(full, n_tiles);
+    int j = 0;
+    for (; j + 1 < n_plain; j += 2) {
+        step(j, P0{}, std::false_type{});
+        step(j + 1, P1{}, std::false_type{});
+    }
+    for (; j < n_tiles; j += 2) {
+        step(j, P0{}, std::true_type{});
+        if (j + 1 < n_tiles) step(j + 1, P1{}, std::true_type{});
     }
 
     // ---- epilogue: O = O_acc / l, lse = M + ln L ----
@@ -486,20 +450,20 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
 }
 
-template <int D, bool CAUSAL, bool PAGED, bool WINDOW = false, int PASS = 0>
+template <int D, bool CAUSAL, bool PAGED, int PASS = 0>
 hipError_t launch_typed(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                         int H, int Hkv, int Nq, int Nk, float scale, PagedKV pg,
-                        hipStream_t stream, Window win = Window{0, 0}) {
+                        hipStream_t stream) {
     using T = Tile<D>;
     const int n_qt = (Nq + T::BM - 1) / T::BM;
     const int BH = B * H;
     const float scale_log2 = scale * kLog2e;
     const float tau_raw = 8.0f / scale_log2;  // move the reference max past +8 in log2 units
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PAGED, WINDOW, PASS>), dim3(n_qt * BH),
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PAGED, PASS>), dim3(n_qt * BH),
                        dim3(T::NT), 0, stream, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                        static_cast<uint16_t*>(o), lse, H, Hkv, Nq, Nk, n_qt, BH, scale_log2,
-                       tau_raw, pg, win);
+                       tau_raw, pg);
     return hipGetLastError();
 }
 
@@ -516,28 +480,14 @@ hipError_t launch_dispatch(const void* q, const void* k, const void* v, void* o,
 
 }  // namespace
 
-hipError_t launch_fwd_bf16_window(const void* q, const void* k, const void* v, void* o,
-                                  float* lse, int B, int H, int Hkv, int Nq, int Nk, int d,
-                                  int window_left, int window_right, float scale,
-                                  hipStream_t stream) {
-    const Window win{window_left < 0 ? kUnbounded : window_left,
-                     window_right < 0 ? kUnbounded : window_right};
-    const PagedKV none{nullptr, nullptr, 0, 0, 0};
-    if (d == 128)
-        return launch_typed<128, false, false, true>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale,
-                                                     none, stream, win);
-    return launch_typed<64, false, false, true>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, none,
-                                                stream, win);
-}
-
 template <int D, bool CAUSAL>
 hipError_t launch_two_pass(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                            int H, int Hkv, int Nq, int Nk, float scale, hipStream_t stream) {
     const PagedKV none{nullptr, nullptr, 0, 0, 0};
-    hipError_t e = launch_typed<D, CAUSAL, false, false, 1>(q, k, v, o, lse, B, H, Hkv, Nq, Nk,
+    hipError_t e = launch_typed<D, CAUSAL, false, 1>(q, k, v, o, lse, B, H, Hkv, Nq, Nk,
                                                             scale, none, stream);
     if (e != hipSuccess) return e;
-    return launch_typed<D, CAUSAL, false, false, 2>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale,
+    return launch_typed<D, CAUSAL, false, 2>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale,
                                                     none, stream);
 }
 

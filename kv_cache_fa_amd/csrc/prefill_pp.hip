@@ -32,6 +32,11 @@
 // * Causal: the work-group visits the key tiles its last row needs; a wave skips the
 //   tiles entirely in its rows' future, and only tiles crossing a wave's diagonal (or
 //   Nk) are masked.
+// * Sliding window (glossary entry "Kayan Pencere Dikkati (Sliding Window Attention)":
+//   query i at position p = Nk - Nq + i attends keys p - left .. p + right): the
+//   work-group visits the band of tiles some row's window touches, a wave computes the
+//   band of its own rows, and only tiles cut by a window edge (or Nk) are masked. A row's
+//   first tile may hold none of its keys, so its reference max can still be -inf there.
 #include <type_traits>
 
 #include "common.h"
@@ -59,12 +64,16 @@ struct TilePP {
     static_assert(DMA >= 1 && DMA * 1024 * NW == TILE, "whole 1 KiB loads per wave");
 };
 
-template <int D, bool CAUSAL>
+// Window sides (keys before / after the query's position); kWinUnbounded for none.
+constexpr int kWinUnbounded = 1 << 29;
+
+template <int D, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                    float* __restrict__ lse, int H, int Hkv, int Nq, int Nk, int n_qt, int BH,
-                   float scale_log2, float tau_raw) {
+                   float scale_log2, float tau_raw, int win_left, int win_right) {
+    static_assert(!(CAUSAL && WINDOW), "a causal window is the window (left, 0)");
     using T = TilePP<D>;
     constexpr int BN = T::BN;
     __shared__ __attribute__((aligned(1024))) char ks0[T::TILE];
@@ -80,7 +89,7 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const int g = lane >> 5;    // which half of the k-slots this lane supplies
 
     int pair, qt;
-    map_work(blockIdx.x, n_qt, BH, H / Hkv, CAUSAL, pair, qt);
+    map_work(blockIdx.x, n_qt, BH, H / Hkv, CAUSAL || WINDOW, pair, qt);
     const int b = pair / H, h = pair % H;
     const int kvh = h / (H / Hkv);
     const int q0 = qt * T::BM;
@@ -98,19 +107,27 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     for (int s = 0; s < T::KS; ++s)
         qf[s] = buf_load16(rq, (uint32_t)(qrow * D + s * 16 + g * 8) * 2);
 
-    // Tiles of the work-group (every wave steps through them for the barriers), tiles
-    // this wave computes (n_w), and the first one it must mask (full_w).
+    // Tiles j0 .. j0 + n_tiles - 1 of the work-group (every wave steps through them for
+    // the barriers), tiles [jw0, jw1) this wave computes, and [jf0, jf1) the ones it can
+    // take unmasked.
     const int n_all = (Nk + BN - 1) / BN;
-    int n_tiles = n_all, n_w = n_all, full_w = Nk / BN;
+    int j0 = 0, n_tiles = n_all, jw0 = 0, jw1 = n_all, jf0 = 0, jf1 = Nk / BN;
+    const int last_row = min(q0 + T::BM, Nq) - 1;
+    const int wlast = min(wrow0 + 31, Nq - 1);
     if (CAUSAL) {
-        const int last_row = min(q0 + T::BM, Nq) - 1;
         n_tiles = min(n_all, (last_row + off) / BN + 1);
-        const int wlast = min(wrow0 + 31, Nq - 1);
-        n_w = wrow0 < Nq ? min(n_all, (wlast + off) / BN + 1) : 0;
-        full_w = min(full_w, (wrow0 + off + 1) / BN);
-    } else if (wrow0 >= Nq) {
-        n_w = 0;
+        jw1 = min(n_all, (wlast + off) / BN + 1);
+        jf1 = min(jf1, (wrow0 + off + 1) / BN);
+    } else if (WINDOW) {
+        j0 = max(0, q0 + off - win_left) / BN;
+        n_tiles = min(Nk - 1, last_row + off + win_right) / BN + 1 - j0;
+        jw0 = max(0, wrow0 + off - win_left) / BN;
+        jw1 = min(Nk - 1, wlast + off + win_right) / BN + 1;
+        // unmasked: every row's window covers the whole tile, which lies below Nk
+        jf0 = max(0, wlast + off - win_left + BN - 1) / BN;
+        jf1 = min(jf1, (wrow0 + off + win_right + 1) / BN);
     }
+    if (wrow0 >= Nq) jw1 = jw0;  // rows past Nq: nothing to compute
 
     // Direct loads: the wave's i-th 1 KiB piece of a tile covers tile bytes
     // [1024 (DMA w + i), +1024); lane L fills byte 16 L of it, i.e. row r, physical chunk
@@ -203,18 +220,33 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 
     // Softmax phase of tile j: mask, running max (lazy reference), P = exp2 into pf.
     auto softmax_phase = [&](const int j) __attribute__((always_inline)) {
-        if (j >= full_w) {
+        if (j < jf0 || j >= jf1) {
             // key offset inside the tile of element (kb, i) is kb*32 + 8*(i/4) + 4g + i%4;
-            // it is dead past the row's last key and past Nk.
+            // it is dead past the row's last key and past Nk (and, for a window, before
+            // the row's first key).
             int lim = Nk - 1 - j * BN - 4 * g;
             if (CAUSAL) lim = min(lim, qrow + off - j * BN - 4 * g);
+            if (WINDOW) {
+                lim = min(lim, qrow + off + win_right - j * BN - 4 * g);
+                const int lo = qrow + off - win_left - j * BN - 4 * g;
 #pragma unroll
-            for (int kb = 0; kb < T::KB; ++kb)
+                for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sacc[kb][i] = -INFINITY;
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = kb * 32 + (i >> 2) * 8 + (i & 3);
+                        if (key > lim || key < lo) sacc[kb][i] = -INFINITY;
+                    }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sacc[kb][i] = -INFINITY;
+            }
         }
-        // Every row attends key 0, so after its first tile the max is finite.
+        // Without a window every row attends key 0, so after its first tile the max is
+        // finite; with one the reference stays -inf until the row's first key, and a row
+        // that does not move keeps alpha = 1 (never -inf - -inf).
         float mx = sacc[0][0];
 #pragma unroll
         for (int kb = 0; kb < T::KB; ++kb)
@@ -235,7 +267,7 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
                 for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
         }
-        const float mb = m_used * scale_log2;
+        const float mb = (WINDOW && m_used == -INFINITY) ? 0.f : m_used * scale_log2;
 #pragma unroll
         for (int t = 0; t < T::PS; ++t) {
             const int kb = t >> 1, base = (t & 1) * 8;
@@ -251,23 +283,25 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    // Period j = slots 2j and 2j+1; K_j is in stage j&1, V_{j-1} in stage (j-1)&1.
+    // Period p = slots 2p and 2p+1 works on tile j = j0 + p; K_j is in stage p&1,
+    // V_{j-1} in stage (p-1)&1.
     //   slot 2j:   A: matrix phase (QK_j, PV_{j-1})   B: softmax of tile j-1
     //   slot 2j+1: B: matrix phase (QK_j, PV_{j-1})   A: softmax of tile j
     // K_{j+1} and V_j are loaded at the start of the period; the barrier that ends it
     // (after each wave's own loads complete) publishes them. The barrier between the two
     // slots waits for nothing but the other group. Each group runs its own copy of the
     // loop (the same number of barriers), straight-line code for one role.
-    auto period = [&](const int j, auto par, auto role) __attribute__((always_inline)) {
+    auto period = [&](const int p, auto par, auto role) __attribute__((always_inline)) {
+        const int j = j0 + p;
         constexpr int pv = decltype(par)::value;
         constexpr bool is_a = decltype(role)::value == 0;
         const char* k_cur = pv ? ks1 : ks0;   // K_j
         char* k_nxt = pv ? ks0 : ks1;         // receives K_{j+1}
         const char* v_prev = pv ? vs0 : vs1;  // V_{j-1}
         char* v_cur = pv ? vs1 : vs0;         // receives V_j
-        if (j + 1 < n_tiles) load_k(j + 1, k_nxt);
-        if (j < n_tiles) load_v(j, v_cur);
-        const bool qk = j < n_w, pvv = j >= 1 && j - 1 < n_w;
+        if (p + 1 < n_tiles) load_k(j + 1, k_nxt);
+        if (p < n_tiles) load_v(j, v_cur);
+        const bool qk = j >= jw0 && j < jw1, pvv = p >= 1 && j - 1 >= jw0 && j - 1 < jw1;
         if constexpr (is_a) {
             matrix_phase(k_cur, v_prev, qk, pvv);
             __builtin_amdgcn_s_barrier();
@@ -280,15 +314,15 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         __syncthreads();
     };
     auto run = [&](auto role) __attribute__((always_inline)) {
-        int j = 0;
-        for (; j + 1 <= n_tiles; j += 2) {
-            period(j, P0{}, role);
-            period(j + 1, P1{}, role);
+        int p = 0;
+        for (; p + 1 <= n_tiles; p += 2) {
+            period(p, P0{}, role);
+            period(p + 1, P1{}, role);
         }
-        if (j <= n_tiles) period(j, P0{}, role);  // periods 0 .. n_tiles
+        if (p <= n_tiles) period(p, P0{}, role);  // periods 0 .. n_tiles
     };
 
-    load_k(0, ks0);
+    load_k(j0, ks0);
     __syncthreads();
     if (grp == 0) run(std::integral_constant<int, 0>{});
     else run(std::integral_constant<int, 1>{});
@@ -312,18 +346,19 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WINDOW>
 hipError_t launch_pp(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                     int H, int Hkv, int Nq, int Nk, float scale, hipStream_t stream) {
+                     int H, int Hkv, int Nq, int Nk, float scale, hipStream_t stream,
+                     int win_left = kWinUnbounded, int win_right = kWinUnbounded) {
     using T = TilePP<D>;
     const int n_qt = (Nq + T::BM - 1) / T::BM;
     const int BH = B * H;
     const float scale_log2 = scale * kLog2e;
     const float tau_raw = 8.0f / scale_log2;  // move the reference max past +8 in log2 units
-    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL>), dim3(n_qt * BH), dim3(T::NT), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, WINDOW>), dim3(n_qt * BH), dim3(T::NT), 0,
+                       stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, H, Hkv,
-                       Nq, Nk, n_qt, BH, scale_log2, tau_raw);
+                       Nq, Nk, n_qt, BH, scale_log2, tau_raw, win_left, win_right);
     return hipGetLastError();
 }
 
@@ -333,10 +368,24 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                            hipStream_t stream) {
     if (d == 128)
-        return causal ? launch_pp<128, true>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream)
-                      : launch_pp<128, false>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream);
-    return causal ? launch_pp<64, true>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream)
-                  : launch_pp<64, false>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream);
+        return causal
+                   ? launch_pp<128, true, false>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream)
+                   : launch_pp<128, false, false>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream);
+    return causal ? launch_pp<64, true, false>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream)
+                  : launch_pp<64, false, false>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream);
+}
+
+hipError_t launch_fwd_bf16_window(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, int B, int H, int Hkv, int Nq, int Nk, int d,
+                                  int window_left, int window_right, float scale,
+                                  hipStream_t stream) {
+    const int left = window_left < 0 ? kWinUnbounded : window_left;
+    const int right = window_right < 0 ? kWinUnbounded : window_right;
+    if (d == 128)
+        return launch_pp<128, false, true>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream,
+                                           left, right);
+    return launch_pp<64, false, true>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream, left,
+                                      right);
 }
 
 }  // namespace kvfa
