@@ -1,8 +1,7 @@
 // bf16 exact attention (prefill) on gfx950 MFMA, fp32 accumulation: the four-wave kernel
-// behind chunked prefill through the page table (fa_fwd_paged) and the two-pass form
-// (fa_fwd_two_pass). Contiguous full / causal and sliding-window prefill (fa_fwd,
-// fa_fwd_window) run the ping-pong kernel of prefill_pp.hip, which does the same
-// arithmetic in the same order.
+// behind the two-pass form (fa_fwd_two_pass). Single-pass prefill (fa_fwd, fa_fwd_window,
+// fa_fwd_paged) runs the ping-pong kernel of prefill_pp.hip; its single pass here
+// (PASS = 0) does the same arithmetic in the same order.
 //
 // Method (page "Donanıma Duyarlı Algoritma Tasarımı: FlashAttention"):
 // * K and V are split into tiles that are staged in LDS, the CU's fast on-chip
@@ -79,31 +78,18 @@ struct Tile {
 // can tell that the loads in flight never alias the stage being read; the work-group
 // barrier that ends tile j (after the loads complete) publishes K_{j+2} and V_{j+1}.
 //
-// Paged K/V (PAGED = true): K and V live in a paged cache [page][16 slots][Hkv][D] and
-// sequence b's token t sits in slot t % 16 of page page_table[b][t / 16]. A 64-key tile
-// is exactly four pages and wave w's direct loads cover tile rows 16w..16w+15, i.e. page
-// 4j + w: each wave needs one page id per tile (fetched a step early) and loads it
-// through a descriptor sized to the page's valid slots, so slots past the sequence (and
-// pages past it or with an out-of-range id) load as zeros and are never read. The keys
-// of sequence b are its seq_lens[b] cached tokens; its Nq queries are the last Nq of them.
-struct PagedKV {
-    const int32_t* page_table;  // [B, max_pages]
-    const int32_t* seq_lens;    // [B]
-    int max_pages, num_pages, max_seq_len;
-};
-
 // Two passes (PASS = 1, then PASS = 2; page "Donanıma Duyarlı Algoritma Tasarımı:
 // FlashAttention", section "FlashAttention-1 (İki Geçişli Yaklaşım)"): the first pass
 // sweeps K only and keeps each row's running max and sum, leaving the row statistics in
 // HBM as lse = M + ln L; the second recomputes the scores, normalises them directly with
 // those statistics (P = exp(scale s - lse)) and accumulates P V, with no rescaling.
-// PASS = 0 is the usual single pass.
-template <int D, bool CAUSAL, bool PAGED, int PASS = 0>
+// PASS = 0 is the usual single pass (not launched by the library).
+template <int D, bool CAUSAL, int PASS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-                     float* __restrict__ lse, int H, int Hkv, int Nq, int Nk_arg, int n_qt,
-                     int BH, float scale_log2, float tau_raw, PagedKV pg) {
+                     float* __restrict__ lse, int H, int Hkv, int Nq, int Nk, int n_qt,
+                     int BH, float scale_log2, float tau_raw) {
     using T = Tile<D>;
     constexpr int BN = T::BN;
     __shared__ __attribute__((aligned(1024))) char ks0[T::TILE];
@@ -117,50 +103,17 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int col = lane & 31;      // query column of S^T / O^T owned by this lane
     const int g = lane >> 5;        // which half of the k-slots this lane supplies
 
-    int pair, qt, b, h;
-    if constexpr (PAGED) {
-        // Sequences of a chunked-prefill batch differ in length, so their work-groups
-        // do too. Work-groups are taken sequence by sequence, longest sequence first
-        // (ranked here from seq_lens for batches of up to 64 sequences; larger batches
-        // keep their order), so the short ones fill in behind the long ones.
-        const int per = H * n_qt, B = BH / H;
-        const int r = blockIdx.x / per;
-        map_work(blockIdx.x - r * per, n_qt, H, H / Hkv, CAUSAL, h, qt);
-        b = r;
-        if (B <= 64) {
-            __shared__ int lens_s[64];
-            __shared__ int pick_s;
-            if (tid < B) lens_s[tid] = pg.seq_lens[tid];
-            __syncthreads();
-            if (tid < B) {
-                const int mine = lens_s[tid];
-                int rank = 0;
-                for (int o = 0; o < B; ++o) {
-                    const int other = lens_s[o];
-                    rank += (other > mine) | ((other == mine) & (o < tid));
-                }
-                if (rank == r) pick_s = tid;
-            }
-            __syncthreads();
-            b = __builtin_amdgcn_readfirstlane(pick_s);
-        }
-        pair = b * H + h;
-    } else {
-        map_work(blockIdx.x, n_qt, BH, H / Hkv, CAUSAL, pair, qt);
-        b = pair / H;
-        h = pair % H;
-    }
+    int pair, qt;
+    map_work(blockIdx.x, n_qt, BH, H / Hkv, CAUSAL, pair, qt);
+    const int b = pair / H, h = pair % H;
     const int kvh = h / (H / Hkv);
     const int q0 = qt * T::BM;
-    int Nk = Nk_arg;
-    if constexpr (PAGED)  // at least the Nq new tokens, at most the table's capacity
-        Nk = __builtin_amdgcn_readfirstlane(min(max(pg.seq_lens[b], Nq), pg.max_seq_len));
     const int off = Nk - Nq;
     const int qrow = q0 + w * 32 + col;
 
     const auto rq = make_rsrc(q + (size_t)pair * Nq * D, (uint32_t)Nq * D * 2);
-    const auto rk = make_rsrc(k + ((size_t)b * Hkv + kvh) * Nk * D, PAGED ? 0u : (uint32_t)Nk * D * 2);
-    const auto rv = make_rsrc(v + ((size_t)b * Hkv + kvh) * Nk * D, PAGED ? 0u : (uint32_t)Nk * D * 2);
+    const auto rk = make_rsrc(k + ((size_t)b * Hkv + kvh) * Nk * D, (uint32_t)Nk * D * 2);
+    const auto rv = make_rsrc(v + ((size_t)b * Hkv + kvh) * Nk * D, (uint32_t)Nk * D * 2);
 
     // B operand of S^T = K Q^T: Q[qrow][16s + 8g .. +7]; rows past Nq load as zero.
     u32x4 qf[T::KS];
@@ -188,63 +141,15 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         dk_off[i] = (uint32_t)(r * T::ROW + ((pc ^ k_swz<D>(r)) * 16));
         dv_off[i] = (uint32_t)(r * T::ROW + ((pc ^ v_swz<D>(r)) * 16));
     }
-    // Paged: the same tile bytes, addressed as slot (tile row - 16w) of the wave's page.
-    const size_t slot_stride = (size_t)Hkv * D;  // elements between consecutive slots
-    uint32_t pk_off[T::DMA], pv_off[T::DMA];
-    if constexpr (PAGED) {
-#pragma unroll
-        for (int i = 0; i < T::DMA; ++i) {
-            const int byte = 1024 * (T::DMA * w + i) + 16 * lane;
-            const int r = byte / T::ROW, pc = (byte % T::ROW) / 16;
-            pk_off[i] = (uint32_t)(((r - 16 * w) * slot_stride) * 2 + ((pc ^ k_swz<D>(r)) * 16));
-            pv_off[i] = (uint32_t)(((r - 16 * w) * slot_stride) * 2 + ((pc ^ v_swz<D>(r)) * 16));
-        }
-    }
-    // Page id of this wave's page in tile j (-1 past the sequence). The table is read
-    // through the constant address space so the uniform load is a scalar one: a vector
-    // load here would make its consumer wait for every tile load issued before it.
-    typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
-    const const_i32_ptr table_row =
-        (const_i32_ptr)(pg.page_table + (PAGED ? (size_t)b * pg.max_pages : 0));
-    auto page_of = [&](int j) -> int {
-        if constexpr (PAGED) {
-            const int pidx = 4 * j + w;
-            if (pidx * 16 >= Nk) return -1;
-            return table_row[pidx];
-        }
-        return -1;
-    };
-    // Descriptor of the wave's page in tile j covering its valid slots (size 0 if none).
-    auto page_rsrc = [&](const uint16_t* cache, int j, int pid) {
-        const int valid = min(16, Nk - (4 * j + w) * 16);
-        const bool ok = valid > 0 && (unsigned)pid < (unsigned)pg.num_pages;
-        const uint16_t* base = cache + ((size_t)(ok ? pid : 0) * 16) * slot_stride + (size_t)kvh * D;
-        return make_rsrc(base, ok ? (uint32_t)(((valid - 1) * slot_stride + D) * 2) : 0u);
-    };
-    int pid_k = page_of(2), pid_v = page_of(1);  // pages of K_{j+2} and V_{j+1} at step 0
     auto load_k = [&](int j, char* dst) {
-        if constexpr (PAGED) {
-            const auto r = page_rsrc(k, j, pid_k);
 #pragma unroll
-            for (int i = 0; i < T::DMA; ++i)
-                buf_load16_lds(r, dst + 1024 * (T::DMA * w + i), pk_off[i], 0u);
-        } else {
-#pragma unroll
-            for (int i = 0; i < T::DMA; ++i)
-                buf_load16_lds(rk, dst + 1024 * (T::DMA * w + i), dk_off[i], (uint32_t)(j * T::TILE));
-        }
+        for (int i = 0; i < T::DMA; ++i)
+            buf_load16_lds(rk, dst + 1024 * (T::DMA * w + i), dk_off[i], (uint32_t)(j * T::TILE));
     };
     auto load_v = [&](int j, char* dst) {
-        if constexpr (PAGED) {
-            const auto r = page_rsrc(v, j, pid_v);
 #pragma unroll
-            for (int i = 0; i < T::DMA; ++i)
-                buf_load16_lds(r, dst + 1024 * (T::DMA * w + i), pv_off[i], 0u);
-        } else {
-#pragma unroll
-            for (int i = 0; i < T::DMA; ++i)
-                buf_load16_lds(rv, dst + 1024 * (T::DMA * w + i), dv_off[i], (uint32_t)(j * T::TILE));
-        }
+        for (int i = 0; i < T::DMA; ++i)
+            buf_load16_lds(rv, dst + 1024 * (T::DMA * w + i), dv_off[i], (uint32_t)(j * T::TILE));
     };
 
     // Per-lane LDS read offsets. K operand (kb, s): row 32 kb + col, logical chunk 2s + g.
@@ -383,10 +288,6 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         char* v_nxt = pv ? vs0 : vs1;   // receives V_{j+1}
         if (j + 2 < n_tiles) load_k(j + 2, k_cur);
         if (PASS != 1 && j + 1 < n_tiles) load_v(j + 1, v_nxt);
-        if constexpr (PAGED) {  // page ids for the next step's loads
-            pid_v = pid_k;
-            pid_k = page_of(j + 3);
-        }
         if (j + 1 < n_tiles) scores(k_nxt, Next{});
         softmax_pv(j, v_cur, par, masked);
         __syncthreads();  // completes the loads above and publishes K_{j+2}, V_{j+1}
@@ -394,22 +295,9 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
     // Prologue: K_0, V_0, K_1 in place; S_0 computed; a barrier separates the S_0 reads
     // from step 0's load into K_0's stage.
-    if constexpr (PAGED) {
-        const int p0 = page_of(0), p1 = page_of(1);
-        const int pk_save = pid_k, pv_save = pid_v;
-        pid_k = p0;
-        pid_v = p0;
-        load_k(0, ks0);
-        load_v(0, vs0);
-        pid_k = p1;
-        if (n_tiles > 1) load_k(1, ks1);
-        pid_k = pk_save;
-        pid_v = pv_save;
-    } else {
-        load_k(0, ks0);
-        if (PASS != 1) load_v(0, vs0);
-        if (n_tiles > 1) load_k(1, ks1);
-    }
+    load_k(0, ks0);
+    if (PASS != 1) load_v(0, vs0);
+    if (n_tiles > 1) load_k(1, ks1);
     __syncthreads();
     scores(ks0, P0{});
     __syncthreads();
@@ -450,32 +338,19 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
 }
 
-template <int D, bool CAUSAL, bool PAGED, int PASS = 0>
+template <int D, bool CAUSAL, int PASS>
 hipError_t launch_typed(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                        int H, int Hkv, int Nq, int Nk, float scale, PagedKV pg,
-                        hipStream_t stream) {
+                        int H, int Hkv, int Nq, int Nk, float scale, hipStream_t stream) {
     using T = Tile<D>;
     const int n_qt = (Nq + T::BM - 1) / T::BM;
     const int BH = B * H;
     const float scale_log2 = scale * kLog2e;
     const float tau_raw = 8.0f / scale_log2;  // move the reference max past +8 in log2 units
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PAGED, PASS>), dim3(n_qt * BH),
-                       dim3(T::NT), 0, stream, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                       static_cast<uint16_t*>(o), lse, H, Hkv, Nq, Nk, n_qt, BH, scale_log2,
-                       tau_raw, pg);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PASS>), dim3(n_qt * BH), dim3(T::NT), 0,
+                       stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, H, Hkv,
+                       Nq, Nk, n_qt, BH, scale_log2, tau_raw);
     return hipGetLastError();
-}
-
-template <bool PAGED>
-hipError_t launch_dispatch(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-                           PagedKV pg, hipStream_t stream) {
-    if (d == 128)
-        return causal ? launch_typed<128, true, PAGED>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, pg, stream)
-                      : launch_typed<128, false, PAGED>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, pg, stream);
-    return causal ? launch_typed<64, true, PAGED>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, pg, stream)
-                  : launch_typed<64, false, PAGED>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, pg, stream);
 }
 
 }  // namespace
@@ -483,12 +358,9 @@ hipError_t launch_dispatch(const void* q, const void* k, const void* v, void* o,
 template <int D, bool CAUSAL>
 hipError_t launch_two_pass(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                            int H, int Hkv, int Nq, int Nk, float scale, hipStream_t stream) {
-    const PagedKV none{nullptr, nullptr, 0, 0, 0};
-    hipError_t e = launch_typed<D, CAUSAL, false, 1>(q, k, v, o, lse, B, H, Hkv, Nq, Nk,
-                                                            scale, none, stream);
+    hipError_t e = launch_typed<D, CAUSAL, 1>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream);
     if (e != hipSuccess) return e;
-    return launch_typed<D, CAUSAL, false, 2>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale,
-                                                    none, stream);
+    return launch_typed<D, CAUSAL, 2>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream);
 }
 
 hipError_t launch_fwd_bf16_two_pass(const void* q, const void* k, const void* v, void* o,
@@ -501,16 +373,5 @@ hipError_t launch_fwd_bf16_two_pass(const void* q, const void* k, const void* v,
                   : launch_two_pass<64, false>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream);
 }
 
-hipError_t launch_fwd_bf16_paged(const void* q, const void* k_cache, const void* v_cache,
-                                 const int32_t* page_table, const int32_t* seq_lens, void* o,
-                                 float* lse, int B, int H, int Hkv, int Nq, int d, int num_pages,
-                                 int max_pages_per_seq, int max_seq_len, int causal, float scale,
-                                 hipStream_t stream) {
-    return launch_dispatch<true>(q, k_cache, v_cache, o, lse, B, H, Hkv, Nq, max_seq_len, d,
-                                 causal, scale,
-                                 PagedKV{page_table, seq_lens, max_pages_per_seq, num_pages,
-                                         max_seq_len},
-                                 stream);
-}
 
 }  // namespace kvfa

@@ -61,6 +61,16 @@ __device__ __forceinline__ void map_work(int id, int n_qt, int BH, int g, bool c
     qt = causal ? n_qt - 1 - r : r;
 }
 
+// Paged K/V: K and V live in a paged cache [page][16 slots][Hkv][D] and sequence b's
+// token t sits in slot t % 16 of page page_table[b][t / 16]. The keys of sequence b are
+// its seq_lens[b] cached tokens (at least the Nq new ones, at most max_seq_len); its Nq
+// queries are the last Nq of them.
+struct PagedKV {
+    const int32_t* page_table;  // [B, max_pages]
+    const int32_t* seq_lens;    // [B]
+    int max_pages, num_pages, max_seq_len;
+};
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Transposing LDS read (ds_read_b64_tr_b16). Within each 16-lane group, source lane

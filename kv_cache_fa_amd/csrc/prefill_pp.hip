@@ -37,6 +37,14 @@
 //   work-group visits the band of tiles some row's window touches, a wave computes the
 //   band of its own rows, and only tiles cut by a window edge (or Nk) are masked. A row's
 //   first tile may hold none of its keys, so its reference max can still be -inf there.
+// * Paged K/V (chunked prefill through the page table, glossary entry "KV Cache
+//   (Anahtar-Değer Önbelleği)": later tokens read the stored K/V of earlier ones): a 64-key
+//   tile is four 16-slot pages and each wave's direct loads cover 8 rows, half a page, so
+//   a wave needs one page id per tile. Ids are read from the table (scalar loads through
+//   the constant address space) a period before their tile is loaded, and each page is
+//   loaded through a descriptor sized to its valid slots: slots past the sequence, pages
+//   past it and out-of-range ids load as zeros and are never read. Sequences differ in
+//   length, so work-groups are taken longest sequence first.
 #include <type_traits>
 
 #include "common.h"
@@ -67,13 +75,15 @@ struct TilePP {
 // Window sides (keys before / after the query's position); kWinUnbounded for none.
 constexpr int kWinUnbounded = 1 << 29;
 
-template <int D, bool CAUSAL, bool WINDOW>
+template <int D, bool CAUSAL, bool WINDOW, bool PAGED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-                   float* __restrict__ lse, int H, int Hkv, int Nq, int Nk, int n_qt, int BH,
-                   float scale_log2, float tau_raw, int win_left, int win_right) {
+                   float* __restrict__ lse, int H, int Hkv, int Nq, int Nk_arg, int n_qt,
+                   int BH, float scale_log2, float tau_raw, int win_left, int win_right,
+                   PagedKV pg) {
     static_assert(!(CAUSAL && WINDOW), "a causal window is the window (left, 0)");
+    static_assert(!(WINDOW && PAGED), "no windowed paged variant");
     using T = TilePP<D>;
     constexpr int BN = T::BN;
     __shared__ __attribute__((aligned(1024))) char ks0[T::TILE];
@@ -88,18 +98,52 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const int col = lane & 31;  // query column of S^T / O^T owned by this lane
     const int g = lane >> 5;    // which half of the k-slots this lane supplies
 
-    int pair, qt;
-    map_work(blockIdx.x, n_qt, BH, H / Hkv, CAUSAL || WINDOW, pair, qt);
-    const int b = pair / H, h = pair % H;
+    int pair, qt, b, h;
+    if constexpr (PAGED) {
+        // Work-groups are taken sequence by sequence, longest sequence first (ranked here
+        // from seq_lens for batches of up to 64 sequences; larger batches keep their
+        // order), so the short ones fill in behind the long ones.
+        const int per = H * n_qt, B = BH / H;
+        const int r = blockIdx.x / per;
+        map_work(blockIdx.x - r * per, n_qt, H, H / Hkv, CAUSAL, h, qt);
+        b = r;
+        if (B <= 64) {
+            __shared__ int lens_s[64];
+            __shared__ int pick_s;
+            if (tid < B) lens_s[tid] = pg.seq_lens[tid];
+            __syncthreads();
+            if (tid < B) {
+                const int mine = lens_s[tid];
+                int rank = 0;
+                for (int o2 = 0; o2 < B; ++o2) {
+                    const int other = lens_s[o2];
+                    rank += (other > mine) | ((other == mine) & (o2 < tid));
+                }
+                if (rank == r) pick_s = tid;
+            }
+            __syncthreads();
+            b = __builtin_amdgcn_readfirstlane(pick_s);
+        }
+        pair = b * H + h;
+    } else {
+        map_work(blockIdx.x, n_qt, BH, H / Hkv, CAUSAL || WINDOW, pair, qt);
+        b = pair / H;
+        h = pair % H;
+    }
     const int kvh = h / (H / Hkv);
     const int q0 = qt * T::BM;
+    int Nk = Nk_arg;
+    if constexpr (PAGED)  // at least the Nq new tokens, at most the table's capacity
+        Nk = __builtin_amdgcn_readfirstlane(min(max(pg.seq_lens[b], Nq), pg.max_seq_len));
     const int off = Nk - Nq;
     const int wrow0 = q0 + w * 32;  // first query row of this wave
     const int qrow = wrow0 + col;
 
     const auto rq = make_rsrc(q + (size_t)pair * Nq * D, (uint32_t)Nq * D * 2);
-    const auto rk = make_rsrc(k + ((size_t)b * Hkv + kvh) * Nk * D, (uint32_t)Nk * D * 2);
-    const auto rv = make_rsrc(v + ((size_t)b * Hkv + kvh) * Nk * D, (uint32_t)Nk * D * 2);
+    const auto rk = make_rsrc(k + (PAGED ? 0 : ((size_t)b * Hkv + kvh) * Nk * D),
+                              PAGED ? 0u : (uint32_t)Nk * D * 2);
+    const auto rv = make_rsrc(v + (PAGED ? 0 : ((size_t)b * Hkv + kvh) * Nk * D),
+                              PAGED ? 0u : (uint32_t)Nk * D * 2);
 
     // B operand of S^T = K Q^T: Q[qrow][16s + 8g .. +7]; rows past Nq load as zero.
     u32x4 qf[T::KS];
@@ -132,23 +176,70 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     // Direct loads: the wave's i-th 1 KiB piece of a tile covers tile bytes
     // [1024 (DMA w + i), +1024); lane L fills byte 16 L of it, i.e. row r, physical chunk
     // pc, with logical chunk pc ^ swizzle(r) of row r.
+    // Paged: row r of the tile is slot r % 16 of page 4j + r / 16 (a wave's rows all lie in
+    // one page), rows of a page being Hkv * D elements apart.
+    static_assert(T::DMA * 1024 / T::ROW == 8, "a wave loads 8 rows of a tile");
+    const size_t slot_stride = (size_t)Hkv * D;
     uint32_t dk_off[T::DMA], dv_off[T::DMA];
 #pragma unroll
     for (int i = 0; i < T::DMA; ++i) {
         const int byte = 1024 * (T::DMA * w + i) + 16 * lane;
         const int r = byte / T::ROW, pc = (byte % T::ROW) / 16;
-        dk_off[i] = (uint32_t)(r * T::ROW + ((pc ^ k_swz<D>(r)) * 16));
-        dv_off[i] = (uint32_t)(r * T::ROW + ((pc ^ v_swz<D>(r)) * 16));
+        const int base = PAGED ? (int)((r % 16) * slot_stride * 2) : r * T::ROW;
+        dk_off[i] = (uint32_t)(base + ((pc ^ k_swz<D>(r)) * 16));
+        dv_off[i] = (uint32_t)(base + ((pc ^ v_swz<D>(r)) * 16));
     }
-    auto load_k = [&](int j, char* dst) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < T::DMA; ++i)
-            buf_load16_lds(rk, dst + 1024 * (T::DMA * w + i), dk_off[i], (uint32_t)(j * T::TILE));
+    // Page id of this wave's page in tile j (-1 past the sequence). The table is read
+    // through the constant address space so the uniform load is a scalar one: a vector
+    // load here would make its consumer wait for every tile load issued before it.
+    typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+    const const_i32_ptr table_row =
+        (const_i32_ptr)(pg.page_table + (PAGED ? (size_t)b * pg.max_pages : 0));
+    const int wpage = w >> 1;  // this wave's page within a tile
+    auto page_of = [&](int j) -> int {
+        if constexpr (PAGED) {
+            const int pidx = 4 * j + wpage;
+            if (pidx * 16 >= Nk) return -1;
+            return table_row[pidx];
+        }
+        return -1;
     };
-    auto load_v = [&](int j, char* dst) __attribute__((always_inline)) {
+    // Descriptor of the wave's page in tile j covering its valid slots (size 0 if none).
+    auto page_rsrc = [&](const uint16_t* cache, int j, int pid) __attribute__((always_inline)) {
+        const int valid = min(16, Nk - (4 * j + wpage) * 16);
+        const bool ok = valid > 0 && (unsigned)pid < (unsigned)pg.num_pages;
+        const uint16_t* base =
+            cache + ((size_t)(ok ? pid : 0) * 16) * slot_stride + (size_t)kvh * D;
+        return make_rsrc(base, ok ? (uint32_t)(((valid - 1) * slot_stride + D) * 2) : 0u);
+    };
+    // pid_cur: page of the tile whose V the current period loads; pid_nxt: of the tile
+    // whose K it loads; pid_fut: read during the period for the next one.
+    int pid_cur = page_of(j0), pid_nxt = page_of(j0 + 1), pid_fut = -1;
+    auto load_k = [&](int j, char* dst, int pid) __attribute__((always_inline)) {
+        if constexpr (PAGED) {
+            const auto r = page_rsrc(k, j, pid);
 #pragma unroll
-        for (int i = 0; i < T::DMA; ++i)
-            buf_load16_lds(rv, dst + 1024 * (T::DMA * w + i), dv_off[i], (uint32_t)(j * T::TILE));
+            for (int i = 0; i < T::DMA; ++i)
+                buf_load16_lds(r, dst + 1024 * (T::DMA * w + i), dk_off[i], 0u);
+        } else {
+#pragma unroll
+            for (int i = 0; i < T::DMA; ++i)
+                buf_load16_lds(rk, dst + 1024 * (T::DMA * w + i), dk_off[i],
+                               (uint32_t)(j * T::TILE));
+        }
+    };
+    auto load_v = [&](int j, char* dst, int pid) __attribute__((always_inline)) {
+        if constexpr (PAGED) {
+            const auto r = page_rsrc(v, j, pid);
+#pragma unroll
+            for (int i = 0; i < T::DMA; ++i)
+                buf_load16_lds(r, dst + 1024 * (T::DMA * w + i), dv_off[i], 0u);
+        } else {
+#pragma unroll
+            for (int i = 0; i < T::DMA; ++i)
+                buf_load16_lds(rv, dst + 1024 * (T::DMA * w + i), dv_off[i],
+                               (uint32_t)(j * T::TILE));
+        }
     };
 
     // Per-lane LDS read offsets. K operand (kb, s): row 32 kb + col, logical chunk 2s + g.
@@ -299,8 +390,9 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         char* k_nxt = pv ? ks0 : ks1;         // receives K_{j+1}
         const char* v_prev = pv ? vs0 : vs1;  // V_{j-1}
         char* v_cur = pv ? vs1 : vs0;         // receives V_j
-        if (p + 1 < n_tiles) load_k(j + 1, k_nxt);
-        if (p < n_tiles) load_v(j, v_cur);
+        if (p + 1 < n_tiles) load_k(j + 1, k_nxt, pid_nxt);
+        if (p < n_tiles) load_v(j, v_cur, pid_cur);
+        if constexpr (PAGED) pid_fut = page_of(j + 2);
         const bool qk = j >= jw0 && j < jw1, pvv = p >= 1 && j - 1 >= jw0 && j - 1 < jw1;
         if constexpr (is_a) {
             matrix_phase(k_cur, v_prev, qk, pvv);
@@ -312,6 +404,10 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             matrix_phase(k_cur, v_prev, qk, pvv);
         }
         __syncthreads();
+        if constexpr (PAGED) {
+            pid_cur = pid_nxt;
+            pid_nxt = pid_fut;
+        }
     };
     auto run = [&](auto role) __attribute__((always_inline)) {
         int p = 0;
@@ -322,7 +418,7 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         if (p <= n_tiles) period(p, P0{}, role);  // periods 0 .. n_tiles
     };
 
-    load_k(j0, ks0);
+    load_k(j0, ks0, pid_cur);
     __syncthreads();
     if (grp == 0) run(std::integral_constant<int, 0>{});
     else run(std::integral_constant<int, 1>{});
@@ -346,19 +442,21 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     }
 }
 
-template <int D, bool CAUSAL, bool WINDOW>
+template <int D, bool CAUSAL, bool WINDOW, bool PAGED = false>
 hipError_t launch_pp(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                      int H, int Hkv, int Nq, int Nk, float scale, hipStream_t stream,
-                     int win_left = kWinUnbounded, int win_right = kWinUnbounded) {
+                     int win_left = kWinUnbounded, int win_right = kWinUnbounded,
+                     PagedKV pg = PagedKV{nullptr, nullptr, 0, 0, 0}) {
     using T = TilePP<D>;
     const int n_qt = (Nq + T::BM - 1) / T::BM;
     const int BH = B * H;
     const float scale_log2 = scale * kLog2e;
     const float tau_raw = 8.0f / scale_log2;  // move the reference max past +8 in log2 units
-    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, WINDOW>), dim3(n_qt * BH), dim3(T::NT), 0,
-                       stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, H, Hkv,
-                       Nq, Nk, n_qt, BH, scale_log2, tau_raw, win_left, win_right);
+    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, WINDOW, PAGED>), dim3(n_qt * BH), dim3(T::NT),
+                       0, stream, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                       static_cast<uint16_t*>(o), lse, H, Hkv, Nq, Nk, n_qt, BH, scale_log2,
+                       tau_raw, win_left, win_right, pg);
     return hipGetLastError();
 }
 
@@ -386,6 +484,25 @@ hipError_t launch_fwd_bf16_window(const void* q, const void* k, const void* v, v
                                            left, right);
     return launch_pp<64, false, true>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream, left,
                                       right);
+}
+
+hipError_t launch_fwd_bf16_paged(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* page_table, const int32_t* seq_lens, void* o,
+                                 float* lse, int B, int H, int Hkv, int Nq, int d, int num_pages,
+                                 int max_pages_per_seq, int max_seq_len, int causal, float scale,
+                                 hipStream_t stream) {
+    const PagedKV pg{page_table, seq_lens, max_pages_per_seq, num_pages, max_seq_len};
+    constexpr int U = kWinUnbounded;
+    if (d == 128)
+        return causal ? launch_pp<128, true, false, true>(q, k_cache, v_cache, o, lse, B, H, Hkv,
+                                                          Nq, max_seq_len, scale, stream, U, U, pg)
+                      : launch_pp<128, false, false, true>(q, k_cache, v_cache, o, lse, B, H,
+                                                           Hkv, Nq, max_seq_len, scale, stream,
+                                                           U, U, pg);
+    return causal ? launch_pp<64, true, false, true>(q, k_cache, v_cache, o, lse, B, H, Hkv, Nq,
+                                                     max_seq_len, scale, stream, U, U, pg)
+                  : launch_pp<64, false, false, true>(q, k_cache, v_cache, o, lse, B, H, Hkv, Nq,
+                                                      max_seq_len, scale, stream, U, U, pg);
 }
 
 }  // namespace kvfa
