@@ -237,7 +237,10 @@ void dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const int qa = q0 + rl + e;
                 bool ok = qa < Nq;
                 if (CAUSAL) ok = ok && key <= qa + off;
-                sa[4 * r + e] = ok ? fast_exp2(fmaf(sa[4 * r + e], scale_log2, -lv[e] * kLog2e)) : 0.f;
+                // computed unconditionally and then selected: a conditional exponential
+                // becomes a branch per element
+                const float ex = fast_exp2(fmaf(sa[4 * r + e], scale_log2, -lv[e] * kLog2e));
+                sa[4 * r + e] = ok ? ex : 0.f;
             }
             const int tt = r >> 1, half = (r & 1) * 2;
             pp[tt][half] = pack_bf16x2(sa[4 * r], sa[4 * r + 1]);
@@ -407,7 +410,8 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const int i = base + 2 * u + e;
                     const int kk = kb * 32 + (i >> 2) * 8 + (i & 3);
                     const bool ok = valid_row && kk <= lim;
-                    const float p = ok ? fast_exp2(fmaf(sa[kb][i], scale_log2, -lse2)) : 0.f;
+                    const float ex = fast_exp2(fmaf(sa[kb][i], scale_log2, -lse2));
+                    const float p = ok ? ex : 0.f;  // selected, not branched
                     sv[e] = p * (pa[kb][i] - drow);
                 }
                 ps[u] = pack_bf16x2(sv[0], sv[1]);
