@@ -78,6 +78,13 @@ def test_fp8_decode_shapes(S, H, Hkv, d, lo, hi):
     _check(inputs.quantize_decode_fp8(base), f"fp8 S{S} H{H} Hkv{Hkv} d{d}")
 
 
+def test_fp8_decode_long_splits():
+    """A large max_seq_len grows the split to 2048 tokens (32 pages per wave); lengths
+    cover one to two splits, d = 64 (one 1 KiB direct load per e4m3 page)."""
+    base = inputs.custom_decode(48, 8, 8, 64, 1, 4096, max_seq_len=32768, seed=322)
+    _check(inputs.quantize_decode_fp8(base), "fp8 long splits")
+
+
 def test_fp8_edge_lengths_and_nan_slots():
     """Empty sequence, page boundaries; unused slots hold e4m3 NaN bytes and the table is
     padded with -1: the output must equal the zero-filled cache's bit for bit."""
