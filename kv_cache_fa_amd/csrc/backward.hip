@@ -381,7 +381,13 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
     for (int i = 0; i < T::DB; ++i) dqa[i] = f32x16{};
 
-    auto tile = [&](int j, const char* kst, const char* vst) {
+    // Tiles below the work-group's first row's diagonal (and below Nk) need no mask when
+    // all its rows exist.
+    int n_plain = q0 + 127 < Nq ? Nk / BN : 0;
+    if (CAUSAL) n_plain = min(n_plain, (q0 + off + 1) / BN);
+
+    auto tile = [&](int j, const char* kst, const char* vst, auto masked)
+                    __attribute__((always_inline)) {
         f32x16 sa[KB], pa[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -409,9 +415,10 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 for (int e = 0; e < 2; ++e) {
                     const int i = base + 2 * u + e;
                     const int kk = kb * 32 + (i >> 2) * 8 + (i & 3);
-                    const bool ok = valid_row && kk <= lim;
                     const float ex = fast_exp2(fmaf(sa[kb][i], scale_log2, -lse2));
-                    const float p = ok ? ex : 0.f;  // selected, not branched
+                    float p = ex;
+                    if constexpr (decltype(masked)::value)
+                        p = (valid_row && kk <= lim) ? ex : 0.f;  // selected, not branched
                     sv[e] = p * (pa[kb][i] - drow);
                 }
                 ps[u] = pack_bf16x2(sv[0], sv[1]);
@@ -424,17 +431,26 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
     };
 
+    // Tile j (stage j & 1) with the next tile's K and V loaded meanwhile.
+    auto step = [&](int j, auto par, auto masked) __attribute__((always_inline)) {
+        constexpr int pv = decltype(par)::value;
+        if (j + 1 < n_tiles) load_kv(j + 1, pv ? ks0 : ks1, pv ? vs0 : vs1);
+        tile(j, pv ? ks1 : ks0, pv ? vs1 : vs0, masked);
+        __syncthreads();
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
     load_kv(0, ks0, vs0);
     __syncthreads();
-    for (int j = 0; j < n_tiles; j += 2) {
-        if (j + 1 < n_tiles) load_kv(j + 1, ks1, vs1);
-        tile(j, ks0, vs0);
-        __syncthreads();
-        if (j + 1 < n_tiles) {
-            if (j + 2 < n_tiles) load_kv(j + 2, ks0, vs0);
-            tile(j + 1, ks1, vs1);
-            __syncthreads();
-        }
+    // Unmasked tiles two at a time (stage parity alternates), then the rest with masking.
+    int j = 0;
+    for (; j + 1 < n_plain; j += 2) {
+        step(j, P0{}, std::false_type{});
+        step(j + 1, P1{}, std::false_type{});
+    }
+    for (; j < n_tiles; j += 2) {
+        step(j, P0{}, std::true_type{});
+        if (j + 1 < n_tiles) step(j + 1, P1{}, std::true_type{});
     }
 
     if (valid_row) {
