@@ -16,22 +16,27 @@
 namespace kvfa {
 namespace {
 
+// Index arithmetic in Idx (32-bit when the chunk count allows: 64-bit division is a long
+// instruction sequence on the GPU). The new rows are loaded before the page-table lookup so
+// the two memory round trips overlap.
+template <typename Idx>
 __global__ __launch_bounds__(256) void kv_append_kernel(
     const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new, u32x4* __restrict__ k_cache,
     u32x4* __restrict__ v_cache, const int32_t* __restrict__ page_table,
-    const int32_t* __restrict__ start_pos, long long n_chunks, int chunks_per_tok, int n_new,
+    const int32_t* __restrict__ start_pos, long long n_chunks_ll, int chunks_per_tok, int n_new,
     int num_pages, int max_pages) {
-    const long long stride = (long long)gridDim.x * blockDim.x;
-    for (long long c = (long long)blockIdx.x * blockDim.x + threadIdx.x; c < n_chunks; c += stride) {
-        const long long tok = c / chunks_per_tok;  // s * n_new + t
-        const int within = (int)(c - tok * chunks_per_tok);
-        const int s = (int)(tok / n_new), t = (int)(tok - (long long)s * n_new);
+    const Idx n_chunks = (Idx)n_chunks_ll;
+    const Idx stride = (Idx)gridDim.x * blockDim.x;
+    for (Idx c = (Idx)blockIdx.x * blockDim.x + threadIdx.x; c < n_chunks; c += stride) {
+        const u32x4 kx = k_new[c], vx = v_new[c];
+        const Idx tok = c / (Idx)chunks_per_tok;  // s * n_new + t
+        const int within = (int)(c - tok * (Idx)chunks_per_tok);
+        const int s = (int)(tok / (Idx)n_new), t = (int)(tok - (Idx)s * n_new);
         const long long pos = (long long)start_pos[s] + t;
         if (pos < 0 || pos >= (long long)max_pages * 16) continue;  // outside the table: dropped
         const int pid = page_table[(size_t)s * max_pages + (int)(pos >> 4)];
         if ((unsigned)pid >= (unsigned)num_pages) continue;  // unassigned page: dropped
         const size_t dst = ((size_t)pid * 16 + (size_t)(pos & 15)) * chunks_per_tok + within;
-        const u32x4 kx = k_new[c], vx = v_new[c];
         k_cache[dst] = kx;
         v_cache[dst] = vx;
     }
@@ -48,10 +53,18 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache,
     // Enough work-groups to cover the chip several times over; the loop strides the rest.
     const long long want = (n_chunks + 255) / 256;
     const int grid = (int)(want < 8192 ? want : 8192);
-    hipLaunchKernelGGL(kv_append_kernel, dim3(grid), dim3(256), 0, stream,
-                       static_cast<const u32x4*>(k_new), static_cast<const u32x4*>(v_new),
-                       static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), page_table,
-                       start_pos, n_chunks, chunks_per_tok, n_new, num_pages, max_pages_per_seq);
+    if (n_chunks + (long long)grid * 256 < (1ll << 31))
+        hipLaunchKernelGGL(kv_append_kernel<int>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<const u32x4*>(k_new), static_cast<const u32x4*>(v_new),
+                           static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache),
+                           page_table, start_pos, n_chunks, chunks_per_tok, n_new, num_pages,
+                           max_pages_per_seq);
+    else
+        hipLaunchKernelGGL(kv_append_kernel<long long>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<const u32x4*>(k_new), static_cast<const u32x4*>(v_new),
+                           static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache),
+                           page_table, start_pos, n_chunks, chunks_per_tok, n_new, num_pages,
+                           max_pages_per_seq);
     return hipGetLastError();
 }
 
