@@ -424,22 +424,37 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     else run(std::integral_constant<int, 1>{});
 
     // ---- epilogue: O = O_acc / l, lse = M + ln L ----
+    // A lane holds 8-byte pieces of its row spread over the row, so the wave first writes
+    // its 32 rows to LDS (the tile stages are free now: every wave has passed the last
+    // period's barrier, and that period loads nothing) and then stores whole rows, each
+    // instruction four full rows of HBM (16-byte chunks XOR-swizzled by row in LDS).
     const float l = l_part + xor32(l_part);
-    if (qrow < Nq) {
-        const float inv = 1.f / l;
-        uint16_t* orow = o + ((size_t)pair * Nq + qrow) * D;
+    const float inv = 1.f / l;
+    constexpr int CH = T::ROW / 16;  // 16-byte chunks per row
+    static_assert(2 * 32 * T::ROW == T::TILE, "two waves' rows fill one stage");
+    char* ost = (w >> 1) == 0 ? ks0 : (w >> 1) == 1 ? ks1 : (w >> 1) == 2 ? vs0 : vs1;
+    ost += (w & 1) * 32 * T::ROW;
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db)
+    for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int d0 = db * 32 + r * 8 + g * 4;
-                u32x2 pk = {pack_bf16x2(oacc[db][r * 4 + 0] * inv, oacc[db][r * 4 + 1] * inv),
-                            pack_bf16x2(oacc[db][r * 4 + 2] * inv, oacc[db][r * 4 + 3] * inv)};
-                *reinterpret_cast<u32x2*>(orow + d0) = pk;
-            }
-        if (lse != nullptr && g == 0)
-            lse[(size_t)pair * Nq + qrow] = (m_used * scale_log2 + fast_log2(l)) * kLn2;
+        for (int r = 0; r < 4; ++r) {
+            // dims 32 db + 8 r + 4 g .. +3: logical chunk 4 db + r, byte 8 g in it
+            const u32x2 pk = {pack_bf16x2(oacc[db][r * 4 + 0] * inv, oacc[db][r * 4 + 1] * inv),
+                              pack_bf16x2(oacc[db][r * 4 + 2] * inv, oacc[db][r * 4 + 3] * inv)};
+            *reinterpret_cast<u32x2*>(ost + col * T::ROW + (((4 * db + r) ^ (col % CH)) * 16) +
+                                      8 * g) = pk;
+        }
+    uint16_t* obase = o + ((size_t)pair * Nq + wrow0) * D;
+#pragma unroll
+    for (int i = 0; i < 32 * T::ROW / 1024; ++i) {
+        const int byte = 1024 * i + 16 * lane;
+        const int row = byte / T::ROW, pc = (byte % T::ROW) / 16;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(ost + byte);
+        if (wrow0 + row < Nq)
+            *reinterpret_cast<u32x4*>(obase + row * D + ((pc ^ (row % CH)) * 8)) = val;
     }
+    if (lse != nullptr && g == 0 && qrow < Nq)
+        lse[(size_t)pair * Nq + qrow] = (m_used * scale_log2 + fast_log2(l)) * kLn2;
 }
 
 template <int D, bool CAUSAL, bool WINDOW, bool PAGED = false>
