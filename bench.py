@@ -360,7 +360,7 @@ def main(argv=None):
 
         # Paged decode on an fp8 (e4m3) copy of the decode workload's cache.
         log("[bench] extra: fp8 paged decode")
-        f8 = inputs.quantize_decode_fp8(dinp)
+        f8 = inputs.quantize_decode_fp8(dinp, seqs=False)
         fkc = torch.from_numpy(f8.k_cache).to(dev)
         fvc = torch.from_numpy(f8.v_cache).to(dev)
         fks = torch.from_numpy(f8.k_scale).to(dev)

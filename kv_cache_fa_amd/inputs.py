@@ -422,21 +422,25 @@ class DecodeFp8Inputs:
     v_seq: list
 
 
-def quantize_decode_fp8(base: DecodeInputs) -> DecodeFp8Inputs:
+def quantize_decode_fp8(base: DecodeInputs, seqs: bool = True) -> DecodeFp8Inputs:
     """Per KV head: scale = max |value| over every cached token / 448, bytes = e4m3(value /
-    scale). Slots past a sequence keep their fill (0 stays 0; NaN fill becomes 0x7f)."""
+    scale). Slots past a sequence keep their fill (0 stays 0; NaN fill becomes 0x7f).
+    seqs=False leaves the per-sequence copies (only a checker needs them) empty."""
     Hkv = base.cfg.Hkv
 
     def quant(cache, seqs):
-        vals = bf16_bits_to_f64(cache)
         amax = np.zeros(Hkv)
         for x in seqs:
             if x.shape[0]:
                 amax = np.maximum(amax, np.abs(bf16_bits_to_f64(x)).max(axis=(0, 2)))
         sc = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32)
-        fin = np.isfinite(vals)
-        q = f64_to_e4m3(np.where(fin, vals / sc[None, None, :, None].astype(np.float64), 0.0))
-        q = np.where(fin, q, np.uint8(0x7F)).astype(np.uint8)
+        div = sc[None, None, :, None].astype(np.float64)
+        q = np.empty(cache.shape, dtype=np.uint8)
+        for p0 in range(0, cache.shape[0], 2048):  # in pieces: the full cache in f64 is GBs
+            vals = bf16_bits_to_f64(cache[p0:p0 + 2048])
+            fin = np.isfinite(vals)
+            part = f64_to_e4m3(np.where(fin, vals / div, 0.0))
+            q[p0:p0 + 2048] = np.where(fin, part, np.uint8(0x7F))
         return q, sc
 
     kq, ks = quant(base.k_cache, base.k_seq)
@@ -445,5 +449,7 @@ def quantize_decode_fp8(base: DecodeInputs) -> DecodeFp8Inputs:
     def quant_seq(x, sc):
         return f64_to_e4m3(bf16_bits_to_f64(x) / sc[None, :, None].astype(np.float64))
 
+    if not seqs:
+        return DecodeFp8Inputs(base, kq, vq, ks, vs, [], [])
     return DecodeFp8Inputs(base, kq, vq, ks, vs, [quant_seq(x, ks) for x in base.k_seq],
                            [quant_seq(x, vs) for x in base.v_seq])
