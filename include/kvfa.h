@@ -141,8 +141,9 @@ int fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float*
  *   o          [num_seqs, H, d] bf16 (written)   lse [num_seqs, H] fp32 (may be NULL)
  *   workspace  device scratch of at least fa_decode_paged_workspace_size(...) bytes,
  *              owned by the caller; its contents on entry do not matter.
- * Work is split over the KV length (split-K); the partial results are merged by their
- * log-sum-exps in a second kernel on the same stream.
+ * Work is split over the KV length (split-K: every work-group reads an equal range of
+ * the cached pages, read from seq_lens on the device); the partial results are merged by
+ * their log-sum-exps in a second kernel on the same stream.
  * Requirements: page_size == 16 and d in {64, 128} (else FA_ERR_UNSUPPORTED);
  * H % Hkv == 0 and H / Hkv <= 16, or a multiple of 16; num_seqs, H, Hkv,
  * num_pages >= 1; max_pages_per_seq * page_size >= max_seq_len >= 1.
@@ -182,8 +183,12 @@ int fa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
                         int num_pages, int max_pages_per_seq, int max_seq_len, float scale,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Tokens of KV one split-K work-group covers for these sizes (a multiple of the page
- * size); the workspace holds ceil(max_seq_len / split) partial results per head. */
+/* The fewest cached tokens one split-K work-group's range holds for these sizes (a
+ * multiple of the page size: 4 pages, or 1/32 of max_seq_len's pages, at most 248 pages).
+ * The cached pages of all sequences, end to end, are cut into equal ranges of at least
+ * this many tokens, one per work-group; a sequence is thereby cut into at most
+ * ceil(max_seq_len / split) + 1 pieces, and the workspace holds that many partial results
+ * per head (plus one int32 per sequence). */
 int fa_decode_paged_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size);
 
 /*

@@ -140,8 +140,10 @@ int decode_checked(const void* q, const void* k_cache, const void* v_cache,
     if (g > 16 && g % 16 != 0) return FA_ERR_UNSUPPORTED;
     if (num_seqs > 65535 || (long long)Hkv * (g > 16 ? g / 16 : 1) > 65535)
         return FA_ERR_UNSUPPORTED;
-    const int T = kvfa::decode_split_tokens(num_seqs, Hkv, max_seq_len, page_size);
-    if ((max_seq_len + (long long)T - 1) / T > 65535) return FA_ERR_UNSUPPORTED;
+    // Pages over all sequences are counted in 32 bits; one grid row per work-group range.
+    if ((long long)num_seqs * ((max_seq_len + page_size - 1) / page_size) >= (1LL << 30) ||
+        kvfa::decode_min_work_groups(num_seqs, max_seq_len) > 65535)
+        return FA_ERR_UNSUPPORTED;
     if (workspace_bytes < kvfa::decode_workspace_bytes(num_seqs, H, Hkv, d, max_seq_len, page_size))
         return FA_ERR_INVALID;
     hipError_t e = kvfa::launch_decode_paged(q, k_cache, v_cache, page_table, seq_lens, o, lse,

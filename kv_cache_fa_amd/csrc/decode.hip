@@ -10,9 +10,15 @@
 // algebra expressed through one log-sum-exp per part).
 //
 // gfx950 mapping (this design):
-// * Work-group = (sequence, KV head, split of `split_tokens` keys), 4 waves; wave w
-//   takes pages w, w+4, ... of its split. All query heads of the GQA group are
-//   served from one read of each K/V page, so every cached byte is read once.
+// * Work-groups per (KV head, head group): the cached pages of all sequences, laid end to
+//   end, are cut into equal ranges of R pages (R from the total, read in-kernel from
+//   seq_lens), one range per work-group, so every work-group reads the same amount and
+//   all of them end together (with one work-group per fixed-size split, the launch ended
+//   with a few long splits running on an otherwise idle chip: a work-group's read rate is
+//   bound by its loads in flight, not shared out). A range may span several sequences; each
+//   piece of a sequence inside it is a segment with its own partial result. 4 waves; wave w
+//   takes pages w, w+4, ... of a segment. All query heads of the GQA group are served from
+//   one read of each K/V page, so every cached byte is read once.
 // * Scores: S^T[token][head] = K_page Q^T with v_mfma_f32_16x16x32_bf16 — one page
 //   (16 tokens) is exactly the MFMA's 16 rows, the group's heads fill its columns.
 //   The MFMA wants one token per lane of a 16-lane group, HBM wants whole rows per
@@ -23,8 +29,10 @@
 // * P.V: plain FMAs. A lane owns one 16-byte chunk of V rows (8 dims) for a subset of
 //   the page's tokens and accumulates all heads of the group; the probabilities reach
 //   it through a small per-wave LDS table.
-// * The split's partial result (normalised O_k, lse_k in log2 units) goes to the
-//   caller's workspace; a second kernel merges the splits in order.
+// * A segment's partial result (normalised O_k, lse_k in log2 units) goes to the
+//   caller's workspace, slot k = its work-group's index among those covering the
+//   sequence; a second kernel merges a sequence's slots in order.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -36,6 +44,26 @@ namespace {
 
 constexpr int kPage = 16;
 constexpr int kWaves = 4;
+// A wave keeps the ids of its pages of a segment in its 64 lanes, plus the two it
+// prefetches past the last one: at most 62 pages per wave and segment.
+constexpr int kMaxRangePages = kWaves * 62;
+// Range plan: a work-group reads at least rmin pages (so a sequence has at most
+// ceil(pages / rmin) + 1 segments: the workspace's slots per head) and at most
+// kMaxRangePages, so at least min_wgs work-groups per (KV head, head group) are launched
+// for the longest possible cache. The kernel uses its target count (set at launch from the
+// resident work-groups), or more when the actual pages need them.
+struct DecodePlan {
+    int rmin, max_slots, min_wgs;
+};
+DecodePlan decode_plan(int num_seqs, int max_seq_len) {
+    const long long max_pages = (max_seq_len + kPage - 1) / kPage;
+    const long long bound = (long long)num_seqs * max_pages;  // pages over all sequences
+    DecodePlan p;
+    p.rmin = (int)std::min<long long>(kMaxRangePages, std::max<long long>(4, (max_pages + 31) / 32));
+    p.max_slots = (int)((max_pages + p.rmin - 1) / p.rmin) + 1;
+    p.min_wgs = (int)std::min<long long>((bound + kMaxRangePages - 1) / kMaxRangePages, 1LL << 30);
+    return p;
+}
 
 // FP8 = true: the cache holds e4m3 bytes with one scale per KV head for K and one for V
 // (dequantised value = byte value x scale). K bytes are converted exactly to bf16 for the
@@ -47,9 +75,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kcache,
     const void* __restrict__ vcache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
-    float* __restrict__ lse_part, int H, int Hkv, int g, int n_hg, int num_pages,
-    int max_pages, int max_seq_len, int split_tokens, int max_splits, float scale_log2_in,
-    const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+    float* __restrict__ lse_part, int* __restrict__ n_slots, int num_seqs, int H, int Hkv,
+    int g, int n_hg, int num_pages, int max_pages, int max_seq_len, int rmin, int max_slots,
+    int wg_target, float scale_log2_in, const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
     constexpr int ES = FP8 ? 1 : 2;    // bytes per cached element
     using KVec = std::conditional_t<FP8, u32x2, u32x4>;  // 8 cached elements
     constexpr int CH = D / 8;          // 16-byte chunks per token row
@@ -77,16 +105,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     __shared__ float red_m[kWaves][GH];
     __shared__ float red_l[kWaves][GH];
 
-    const int s = blockIdx.z;
     const int kvh = blockIdx.x / n_hg, hg = blockIdx.x % n_hg;
-    const int split = blockIdx.y;
-    const int L = min(max(seq_lens[s], 0), max_seq_len);
-    const int t0 = split * split_tokens;
-    if (t0 >= L) return;  // uniform: this split holds no cached token
-    const int t1 = min(t0 + split_tokens, L);
-    const int first_page = t0 / kPage;
-    const int n_pg = (t1 - t0 + kPage - 1) / kPage;
-
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
     const int n = lane & 15;     // head column of S^T held by this lane
@@ -104,32 +123,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     // Move the reference max past +8 in log2 units (with a zero K scale every score is 0:
     // the first page then moves the reference and every later one keeps it).
     const float tau_raw = scale_log2 > 0.f ? 8.0f / scale_log2 : 0.f;
-
-    // B operand (Q^T): Q[s][h0+n][8*(4j + kq) .. +7], zero for padding columns.
-    u32x4 qf[KS];
-#pragma unroll
-    for (int j = 0; j < KS; ++j) {
-        qf[j] = u32x4{0, 0, 0, 0};
-        if (n < nheads)
-            qf[j] = *reinterpret_cast<const u32x4*>(q + ((size_t)s * H + h0 + n) * D +
-                                                     (j * 4 + kq) * 8);
-    }
-
-    float m_used = -INFINITY, l_part = 0.f;
-    float oacc[GH][8];
-#pragma unroll
-    for (int hh = 0; hh < GH; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) oacc[hh][e] = 0.f;
-
-    // This wave's pages are first_page + w + kWaves*i, i < n_my. Lane i holds the
-    // physical id of the i-th one, so no page-table load sits on the loop's critical path.
-    const int n_my = w < n_pg ? (n_pg - w + kWaves - 1) / kWaves : 0;
-    int pid_lane = -1;
-    if (lane < n_my) pid_lane = page_table[(size_t)s * max_pages + first_page + w + kWaves * lane];
-    // Let the ids arrive once, here; afterwards the register no longer counts as a pending
-    // load, so reading it inside the loop does not wait for the page loads in flight.
-    __asm__ volatile("" : "+v"(pid_lane));
 
     // Issue the loads of the wave's it-th page (K rows as the MFMA A operand, V chunks for
     // the P.V lanes). Returns false for an out-of-range page id, which is never read.
@@ -160,6 +153,37 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         if constexpr (FP8) return buf_load8_nt(r, off);
         else return buf_load16_nt(r, off);
     };
+    // One segment: pages [first_page, first_page + n_pg) of sequence s (L cached tokens),
+    // partial result into slot `slot`.
+    auto segment = [&](const int s, const int L, const int first_page, const int n_pg,
+                       const int slot) __attribute__((always_inline)) {
+    const int t1 = min((first_page + n_pg) * kPage, L);
+    // B operand (Q^T): Q[s][h0+n][8*(4j + kq) .. +7], zero for padding columns.
+    u32x4 qf[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+        qf[j] = u32x4{0, 0, 0, 0};
+        if (n < nheads)
+            qf[j] = *reinterpret_cast<const u32x4*>(q + ((size_t)s * H + h0 + n) * D +
+                                                     (j * 4 + kq) * 8);
+    }
+
+    float m_used = -INFINITY, l_part = 0.f;
+    float oacc[GH][8];
+#pragma unroll
+    for (int hh = 0; hh < GH; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oacc[hh][e] = 0.f;
+
+    // This wave's pages are first_page + w + kWaves*i, i < n_my. Lane i holds the
+    // physical id of the i-th one, so no page-table load sits on the loop's critical path.
+    const int n_my = w < n_pg ? (n_pg - w + kWaves - 1) / kWaves : 0;
+    int pid_lane = -1;
+    if (lane < n_my) pid_lane = page_table[(size_t)s * max_pages + first_page + w + kWaves * lane];
+    // Let the ids arrive once, here; afterwards the register no longer counts as a pending
+    // load, so reading it inside the loop does not wait for the page loads in flight.
+    __asm__ volatile("" : "+v"(pid_lane));
+
     auto load_page = [&](int it, char* kst, KVec (&vv)[TPL]) -> bool {
         const int pid = __builtin_amdgcn_readlane(pid_lane, it);
         const bool valid = (unsigned)pid < (unsigned)num_pages;
@@ -315,14 +339,60 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
                 acc = fmaf(f, red_o(ww)[hh * D + dd], acc);
             }
         }
-        const size_t row = ((size_t)s * H + h0 + hh) * max_splits + split;
+        const size_t row = ((size_t)s * H + h0 + hh) * max_slots + slot;
         o_part[row * D + dd] = M != -INFINITY ? acc / lsum * v_sc : 0.f;
         if (dd == 0)
             lse_part[row] = M != -INFINITY ? M * scale_log2 + fast_log2(lsum) : -INFINITY;
     }
+    __syncthreads();  // the next segment's loads overwrite the merge buffers
+    };
+
+    // ---- the work-group's range of pages, and the segments in it ----
+    // Pages of all sequences end to end (per KV head): sequence s holds [S_s, S_s + P_s).
+    // Every wave computes the same plan from the lengths.
+    int P_tot = 0;
+    for (int c0 = 0; c0 < num_seqs; c0 += 64) {
+        const int Ls = c0 + lane < num_seqs ? min(max(seq_lens[c0 + lane], 0), max_seq_len) : 0;
+        int p = (Ls + kPage - 1) / kPage;
+#pragma unroll
+        for (int msk = 1; msk < 64; msk <<= 1) p += __shfl_xor(p, msk, 64);
+        P_tot += __builtin_amdgcn_readfirstlane(p);
+    }
+    // Work-groups in use: the target, or as many as keep R <= kMaxRangePages (at most the
+    // launched ones, which suffice for the longest possible cache); the rest return.
+    const int n_wg = min((int)gridDim.y, max(wg_target, (P_tot + kMaxRangePages - 1) / kMaxRangePages));
+    const int R = max(rmin, (P_tot + n_wg - 1) / n_wg);
+    const int g0 = (int)blockIdx.y * R;
+    if (g0 >= P_tot) return;  // uniform: nothing left for this work-group
+    const int g1 = min(g0 + R, P_tot);
+    int base = 0;  // pages of the sequences before the current 64
+    for (int c0 = 0; c0 < num_seqs && base < g1; c0 += 64) {
+        const int Ls = c0 + lane < num_seqs ? min(max(seq_lens[c0 + lane], 0), max_seq_len) : 0;
+        const int Ps = (Ls + kPage - 1) / kPage;
+        int x = Ps;  // inclusive prefix sum over the lanes
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        const int S = base + x - Ps;
+        unsigned long long segs = __builtin_amdgcn_ballot_w64(Ps > 0 && S < g1 && S + Ps > g0);
+        while (segs) {
+            const int ln = __builtin_ctzll(segs);
+            segs &= segs - 1;
+            const int Ss = __builtin_amdgcn_readlane(S, ln);
+            const int Pq = __builtin_amdgcn_readlane(Ps, ln);
+            const int a = max(g0, Ss) - Ss, b = min(g1, Ss + Pq) - Ss;
+            const int slot = (int)blockIdx.y - Ss / R;
+            // The first work-group of a sequence records how many slots it has.
+            if (slot == 0 && tid == 0) n_slots[c0 + ln] = (Ss + Pq - 1) / R - Ss / R + 1;
+            segment(c0 + ln, __builtin_amdgcn_readlane(Ls, ln), a, b - a, slot);
+        }
+        base += __builtin_amdgcn_readlane(x, 63);
+    }
 }
 
-// Merge the splits of each (sequence, head): LSE = log2 sum_k 2^lse_k (relative to the
+// Merge the slots of each (sequence, head): LSE = log2 sum_k 2^lse_k (relative to the
 // largest), O = sum_k 2^(lse_k - LSE) O_k. One wave per (sequence, head), kCombineHeads
 // heads per work-group. The split statistics are spread over the lanes (one split per
 // lane, wave reductions for the max and the sum); each lane then owns D/64 output dims and
@@ -332,17 +402,17 @@ constexpr int kCombineHeads = 4;
 template <int D>
 __global__ __launch_bounds__(64 * kCombineHeads) void decode_combine_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part,
-    const int32_t* __restrict__ seq_lens, uint16_t* __restrict__ o, float* __restrict__ lse,
-    int H, int max_seq_len, int split_tokens, int max_splits) {
+    const int* __restrict__ n_slots, const int32_t* __restrict__ seq_lens,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int H, int max_seq_len, int max_slots) {
     constexpr int PER = D / 64;  // output dims per lane (2 or 1)
     const int s = blockIdx.y, lane = threadIdx.x & 63;
     const int h = blockIdx.x * kCombineHeads + (threadIdx.x >> 6);
     if (h >= H) return;  // uniform per wave
     const int L = min(max(seq_lens[s], 0), max_seq_len);
-    const int ns = (L + split_tokens - 1) / split_tokens;
+    const int ns = L > 0 ? n_slots[s] : 0;  // no slot was written for an empty sequence
     const size_t row = (size_t)s * H + h;
-    const float* lp = lse_part + row * max_splits;
-    const float* op = o_part + row * max_splits * D + lane * PER;
+    const float* lp = lse_part + row * max_slots;
+    const float* op = o_part + row * max_slots * D + lane * PER;
 
     float m = -INFINITY;
     for (int k = lane; k < ns; k += 64) m = fmaxf(m, lp[k]);
@@ -407,68 +477,89 @@ __global__ __launch_bounds__(64 * kCombineHeads) void decode_combine_kernel(
         lse[row] = M != -INFINITY ? (M + fast_log2(wsum)) * kLn2 : -INFINITY;
 }
 
+// Workspace: o_part [num_seqs, H, max_slots, D] fp32, lse_part [num_seqs, H, max_slots]
+// fp32, n_slots [num_seqs] int32.
+struct DecodeWorkspace {
+    float* o_part;
+    float* lse_part;
+    int* n_slots;
+};
+DecodeWorkspace decode_workspace(void* ws, int num_seqs, int H, int d, int max_slots) {
+    const size_t rows = (size_t)num_seqs * H * max_slots;
+    float* o_part = static_cast<float*>(ws);
+    float* lse_part = o_part + rows * d;
+    return {o_part, lse_part, reinterpret_cast<int*>(lse_part + rows)};
+}
+
 template <int D, int GH, bool FP8>
 hipError_t launch_split(const void* q, const void* kc, const void* vc, const int32_t* pt,
-                        const int32_t* sl, float* o_part, float* lse_part, int num_seqs, int H,
-                        int Hkv, int g, int n_hg, int num_pages, int max_pages, int max_seq_len,
-                        int split_tokens, int max_splits, float scale, const float* k_scale,
+                        const int32_t* sl, const DecodeWorkspace& ws, const DecodePlan& plan,
+                        int num_seqs, int H, int Hkv, int g, int n_hg, int num_pages,
+                        int max_pages, int max_seq_len, float scale, const float* k_scale,
                         const float* v_scale, hipStream_t stream) {
     const float scale_log2 = scale * kLog2e;
-    // KV heads vary fastest: the work-groups covering one token range of one sequence
-    // are dispatched together, so each physical page (all KV heads of 16 slots, contiguous)
-    // is read by concurrently running work-groups.
-    dim3 grid(Hkv * n_hg, max_splits, num_seqs);
+    // Target: one round of resident work-groups (two for an fp8 cache, whose ranges take
+    // half the time) shared by the (KV head, head group) pairs.
+    static const int per_cu = [] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<D, GH, FP8>,
+                                                         256, 0) != hipSuccess)
+            n = 1;
+        return std::max(1, n);
+    }();
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipErrorInvalidDevice;
+    const int groups = Hkv * n_hg;
+    const int target = std::max(1, per_cu * std::max(1, cus) * (FP8 ? 2 : 1) / groups);
+    // KV heads vary fastest: the work-groups covering one page range are dispatched
+    // together, so each physical page (all KV heads of 16 slots, contiguous) is read by
+    // concurrently running work-groups.
+    dim3 grid(groups, std::max(target, plan.min_wgs));
     hipLaunchKernelGGL((decode_split_kernel<D, GH, FP8>), grid, dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(q), kc, vc, pt, sl, o_part, lse_part, H, Hkv,
-                       g, n_hg, num_pages, max_pages, max_seq_len, split_tokens, max_splits,
-                       scale_log2, k_scale, v_scale);
+                       static_cast<const uint16_t*>(q), kc, vc, pt, sl, ws.o_part, ws.lse_part,
+                       ws.n_slots, num_seqs, H, Hkv, g, n_hg, num_pages, max_pages, max_seq_len,
+                       plan.rmin, plan.max_slots, target, scale_log2, k_scale, v_scale);
     return hipGetLastError();
 }
 
 template <int D, bool FP8>
 hipError_t launch_split_d(int GH, const void* q, const void* kc, const void* vc,
-                          const int32_t* pt, const int32_t* sl, float* o_part, float* lse_part,
-                          int num_seqs, int H, int Hkv, int g, int n_hg, int num_pages,
-                          int max_pages, int max_seq_len, int split_tokens, int max_splits,
-                          float scale, const float* ks, const float* vs, hipStream_t stream) {
+                          const int32_t* pt, const int32_t* sl, const DecodeWorkspace& ws,
+                          const DecodePlan& plan, int num_seqs, int H, int Hkv, int g, int n_hg,
+                          int num_pages, int max_pages, int max_seq_len, float scale,
+                          const float* ks, const float* vs, hipStream_t stream) {
     if (GH == 4)
-        return launch_split<D, 4, FP8>(q, kc, vc, pt, sl, o_part, lse_part, num_seqs, H, Hkv, g,
-                                       n_hg, num_pages, max_pages, max_seq_len, split_tokens,
-                                       max_splits, scale, ks, vs, stream);
+        return launch_split<D, 4, FP8>(q, kc, vc, pt, sl, ws, plan, num_seqs, H, Hkv, g, n_hg,
+                                       num_pages, max_pages, max_seq_len, scale, ks, vs, stream);
     if (GH == 8)
-        return launch_split<D, 8, FP8>(q, kc, vc, pt, sl, o_part, lse_part, num_seqs, H, Hkv, g,
-                                       n_hg, num_pages, max_pages, max_seq_len, split_tokens,
-                                       max_splits, scale, ks, vs, stream);
-    return launch_split<D, 16, FP8>(q, kc, vc, pt, sl, o_part, lse_part, num_seqs, H, Hkv, g,
-                                    n_hg, num_pages, max_pages, max_seq_len, split_tokens,
-                                    max_splits, scale, ks, vs, stream);
+        return launch_split<D, 8, FP8>(q, kc, vc, pt, sl, ws, plan, num_seqs, H, Hkv, g, n_hg,
+                                       num_pages, max_pages, max_seq_len, scale, ks, vs, stream);
+    return launch_split<D, 16, FP8>(q, kc, vc, pt, sl, ws, plan, num_seqs, H, Hkv, g, n_hg,
+                                    num_pages, max_pages, max_seq_len, scale, ks, vs, stream);
 }
 
 }  // namespace
 
 int decode_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size) {
-    // A work-group has a fixed cost (page ids, first loads, merging its waves, writing
-    // its partial result) and the last round of work-groups leaves CUs idle. Splits of 512
-    // tokens are lengthened (in steps of 128) while the launch would exceed about six
-    // rounds of resident work-groups (256 CUs x 4), and shortened when fewer than 2048
-    // work-groups would be launched. (T <= 2048 keeps every wave's page count, plus the
-    // two pages it prefetches past its last one, within the 64 lanes that hold its page
-    // ids.)
-    constexpr long long kResident = 256 * 4;
-    auto wgs = [&](int T) { return (long long)num_seqs * Hkv * ((max_seq_len + T - 1) / T); };
-    int T = 512;
-    while (T < 2048 && wgs(T) > 6 * kResident) T += 128;
-    while (T > 64 && wgs(T) < 2048) T >>= 1;
-    if (T < page_size) T = page_size;
-    return T;
+    (void)page_size;
+    (void)Hkv;
+    return decode_plan(num_seqs, max_seq_len).rmin * kPage;
+}
+
+int decode_min_work_groups(int num_seqs, int max_seq_len) {
+    return decode_plan(num_seqs, max_seq_len).min_wgs;
 }
 
 size_t decode_workspace_bytes(int num_seqs, int H, int Hkv, int d, int max_seq_len,
                               int page_size) {
-    const int T = decode_split_tokens(num_seqs, Hkv, max_seq_len, page_size);
-    const size_t max_splits = (size_t)(max_seq_len + T - 1) / T;
-    const size_t rows = (size_t)num_seqs * H * max_splits;
-    return rows * (size_t)d * sizeof(float) + rows * sizeof(float);
+    (void)page_size;
+    (void)Hkv;
+    const DecodePlan plan = decode_plan(num_seqs, max_seq_len);
+    const size_t rows = (size_t)num_seqs * H * plan.max_slots;
+    return rows * (size_t)d * sizeof(float) + rows * sizeof(float) +
+           (size_t)num_seqs * sizeof(int);
 }
 
 hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -478,43 +569,41 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
                                void* workspace, hipStream_t stream, const float* k_scale,
                                const float* v_scale) {
     const bool fp8 = k_scale != nullptr;
-    const int T = decode_split_tokens(num_seqs, Hkv, max_seq_len, kPage);
-    const int max_splits = (max_seq_len + T - 1) / T;
     const int g = H / Hkv;
     const int GH = g <= 4 ? 4 : g <= 8 ? 8 : 16;
     const int n_hg = g <= 16 ? 1 : g / 16;
-    float* o_part = static_cast<float*>(workspace);
-    float* lse_part = o_part + (size_t)num_seqs * H * max_splits * d;
+    const DecodePlan plan = decode_plan(num_seqs, max_seq_len);
+    const DecodeWorkspace ws = decode_workspace(workspace, num_seqs, H, d, plan.max_slots);
 
     hipError_t e;
     if (d == 128)
-        e = fp8 ? launch_split_d<128, true>(GH, q, k_cache, v_cache, page_table, seq_lens, o_part,
-                                            lse_part, num_seqs, H, Hkv, g, n_hg, num_pages,
-                                            max_pages_per_seq, max_seq_len, T, max_splits, scale,
-                                            k_scale, v_scale, stream)
-                : launch_split_d<128, false>(GH, q, k_cache, v_cache, page_table, seq_lens,
-                                             o_part, lse_part, num_seqs, H, Hkv, g, n_hg,
-                                             num_pages, max_pages_per_seq, max_seq_len, T,
-                                             max_splits, scale, nullptr, nullptr, stream);
+        e = fp8 ? launch_split_d<128, true>(GH, q, k_cache, v_cache, page_table, seq_lens, ws,
+                                            plan, num_seqs, H, Hkv, g, n_hg, num_pages,
+                                            max_pages_per_seq, max_seq_len, scale, k_scale,
+                                            v_scale, stream)
+                : launch_split_d<128, false>(GH, q, k_cache, v_cache, page_table, seq_lens, ws,
+                                             plan, num_seqs, H, Hkv, g, n_hg, num_pages,
+                                             max_pages_per_seq, max_seq_len, scale, nullptr,
+                                             nullptr, stream);
     else
-        e = fp8 ? launch_split_d<64, true>(GH, q, k_cache, v_cache, page_table, seq_lens, o_part,
-                                           lse_part, num_seqs, H, Hkv, g, n_hg, num_pages,
-                                           max_pages_per_seq, max_seq_len, T, max_splits, scale,
-                                           k_scale, v_scale, stream)
-                : launch_split_d<64, false>(GH, q, k_cache, v_cache, page_table, seq_lens,
-                                            o_part, lse_part, num_seqs, H, Hkv, g, n_hg,
-                                            num_pages, max_pages_per_seq, max_seq_len, T,
-                                            max_splits, scale, nullptr, nullptr, stream);
+        e = fp8 ? launch_split_d<64, true>(GH, q, k_cache, v_cache, page_table, seq_lens, ws,
+                                           plan, num_seqs, H, Hkv, g, n_hg, num_pages,
+                                           max_pages_per_seq, max_seq_len, scale, k_scale,
+                                           v_scale, stream)
+                : launch_split_d<64, false>(GH, q, k_cache, v_cache, page_table, seq_lens, ws,
+                                            plan, num_seqs, H, Hkv, g, n_hg, num_pages,
+                                            max_pages_per_seq, max_seq_len, scale, nullptr,
+                                            nullptr, stream);
     if (e != hipSuccess) return e;
     dim3 grid((H + kCombineHeads - 1) / kCombineHeads, num_seqs);
     if (d == 128)
         hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(64 * kCombineHeads), 0, stream,
-                           o_part, lse_part, seq_lens, static_cast<uint16_t*>(o), lse, H,
-                           max_seq_len, T, max_splits);
+                           ws.o_part, ws.lse_part, ws.n_slots, seq_lens,
+                           static_cast<uint16_t*>(o), lse, H, max_seq_len, plan.max_slots);
     else
         hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(64 * kCombineHeads), 0, stream,
-                           o_part, lse_part, seq_lens, static_cast<uint16_t*>(o), lse, H,
-                           max_seq_len, T, max_splits);
+                           ws.o_part, ws.lse_part, ws.n_slots, seq_lens,
+                           static_cast<uint16_t*>(o), lse, H, max_seq_len, plan.max_slots);
     return hipGetLastError();
 }
 

@@ -46,6 +46,7 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
 
 // Decode split plan: tokens per split-K work-group, and the workspace it implies.
 int decode_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size);
+int decode_min_work_groups(int num_seqs, int max_seq_len);
 size_t decode_workspace_bytes(int num_seqs, int H, int Hkv, int d, int max_seq_len,
                               int page_size);
 

@@ -195,12 +195,15 @@ def test_workspace_size(lib):
     assert f(0, 32, 8, 128, 8192, 16) == 0
     assert f(64, 32, 8, 100, 8192, 16) == 0
     assert f(64, 32, 8, 128, 8192, 8) == 0
+    # fewest cached tokens a work-group's range holds: 4 pages, or 1/32 of the longest
+    # possible sequence, at most 248 pages (62 per wave)
     T = lib.fa_decode_paged_split_tokens(64, 8, 8192, 16)
-    assert T % 16 == 0 and T >= 16
-    splits = -(-8192 // T)
-    assert f(64, 32, 8, 128, 8192, 16) == 64 * 32 * splits * (128 + 1) * 4
-    # few sequences: shorter splits keep enough work-groups in flight
-    assert lib.fa_decode_paged_split_tokens(1, 1, 8192, 16) < T
+    assert T == 16 * 16
+    slots = -(-8192 // T) + 1  # segments a sequence can be cut into
+    assert f(64, 32, 8, 128, 8192, 16) == 64 * 32 * slots * (128 + 1) * 4 + 64 * 4
+    assert lib.fa_decode_paged_split_tokens(1, 1, 100, 16) == 4 * 16
+    assert lib.fa_decode_paged_split_tokens(1, 1, 131072, 16) == 248 * 16
+    assert lib.fa_decode_paged_split_tokens(1, 1, 1 << 30, 16) == 248 * 16
 
 
 def test_binding_refuses_host_tensors():

@@ -59,14 +59,15 @@ def test_decode_shapes(S, H, Hkv, d, lo, hi):
     _check(inp, f"decode S{S} H{H} Hkv{Hkv} d{d}")
 
 
-def test_decode_long_splits():
-    """A large max_seq_len grows the split to its 2048-token maximum (32 pages per wave
-    plus the two prefetched past the end, all within the page-id lanes); the actual
-    lengths cover one to two splits."""
+def test_decode_long_ranges():
+    """max_seq_len 131072 makes every work-group's range 248 pages (62 per wave: a wave's
+    page ids fill lanes 0-61 and the two pages it prefetches past its last one lanes
+    62-63); the long sequence spans 34 ranges, the others begin and end inside ranges."""
     from kv_cache_fa_amd import _lib
-    assert _lib.fa_decode_paged_split_tokens(48, 8, 32768, 16) == 2048
-    inp = inputs.custom_decode(48, 8, 8, 64, 1, 4096, max_seq_len=32768, seed=321)
-    _check(inp, "decode long splits")
+    assert _lib.fa_decode_paged_split_tokens(3, 1, 131072, 16) == 248 * 16
+    cfg = inputs.DecodeConfig("long", 3, 4, 1, 64, 0, 0, 16, 131072, 1 / 8, 5)
+    inp = inputs.make_decode(cfg, seq_lens=[131072, 4000, 70001])
+    _check(inp, "decode long ranges")
 
 
 def test_decode_edge_lengths():

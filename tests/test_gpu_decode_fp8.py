@@ -78,11 +78,12 @@ def test_fp8_decode_shapes(S, H, Hkv, d, lo, hi):
     _check(inputs.quantize_decode_fp8(base), f"fp8 S{S} H{H} Hkv{Hkv} d{d}")
 
 
-def test_fp8_decode_long_splits():
-    """A large max_seq_len grows the split to 2048 tokens (32 pages per wave); lengths
-    cover one to two splits, d = 64 (one 1 KiB direct load per e4m3 page)."""
-    base = inputs.custom_decode(48, 8, 8, 64, 1, 4096, max_seq_len=32768, seed=322)
-    _check(inputs.quantize_decode_fp8(base), "fp8 long splits")
+def test_fp8_decode_long_ranges():
+    """Work-group ranges of 248 pages (62 per wave) on an e4m3 cache, d = 64 (one 1 KiB
+    direct load per page); one sequence spans 34 ranges."""
+    cfg = inputs.DecodeConfig("long", 3, 4, 1, 64, 0, 0, 16, 131072, 1 / 8, 6)
+    base = inputs.make_decode(cfg, seq_lens=[131072, 4000, 70001])
+    _check(inputs.quantize_decode_fp8(base), "fp8 long ranges")
 
 
 def test_fp8_edge_lengths_and_nan_slots():
