@@ -53,6 +53,11 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m kv_cache_fa_amd.build` (hipcc, gfx950)")
+        # torch's HIP and HSA runtimes load first: the library's own HIP runtime then runs
+        # on the HSA runtime torch already loaded. Loaded the other way round (the library
+        # before torch), the library's runtime found no device once torch had initialised
+        # the GPU.
+        import torch  # noqa: F401
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)

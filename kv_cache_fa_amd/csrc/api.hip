@@ -3,6 +3,8 @@
 // call enqueues nothing and touches no output.
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include "../../include/kvfa.h"
 #include "launch.h"
@@ -10,6 +12,16 @@
 namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Status of a launch. With KVFA_DEBUG set in the environment, a HIP failure is also
+// described on stderr (the C status only says that HIP failed).
+int hip_status(hipError_t e, const char* fn) {
+    if (e == hipSuccess) return FA_OK;
+    if (getenv("KVFA_DEBUG") != nullptr)
+        fprintf(stderr, "kvfa: %s: HIP error %d (%s): %s\n", fn, (int)e, hipGetErrorName(e),
+                hipGetErrorString(e));
+    return FA_ERR_HIP;
+}
 
 // Shared checks of the two prefill entry points.
 int check_prefill(const void* q, const void* k, const void* v, const void* o, const void* lse,
@@ -50,7 +62,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     if (n_wg >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
     hipError_t e = kvfa::launch_fwd_bf16(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal != 0, scale,
                                          static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return hip_status(e, "fa_fwd");
 }
 
 int fa_fwd_two_pass(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -64,7 +76,7 @@ int fa_fwd_two_pass(const void* q, const void* k, const void* v, void* o, float*
     hipError_t e = kvfa::launch_fwd_bf16_two_pass(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d,
                                                   causal != 0, scale,
                                                   static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return hip_status(e, "fa_fwd_two_pass");
 }
 
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -79,7 +91,7 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
     hipError_t e = kvfa::launch_fwd_bf16_window(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d,
                                                 window_left, window_right, scale,
                                                 static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return hip_status(e, "fa_fwd_window");
 }
 
 int fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
@@ -89,7 +101,7 @@ int fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float*
     if (H > 65535 || B > 65535) return FA_ERR_UNSUPPORTED;
     hipError_t e = kvfa::launch_fwd_fp32(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal != 0, scale,
                                          static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return hip_status(e, "fa_fwd_fp32");
 }
 
 int fa_decode_paged_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size) {
@@ -150,7 +162,7 @@ int decode_checked(const void* q, const void* k_cache, const void* v_cache,
                                              num_seqs, H, Hkv, d, num_pages, max_pages_per_seq,
                                              max_seq_len, scale, workspace,
                                              static_cast<hipStream_t>(stream), k_scale, v_scale);
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return hip_status(e, "decode_checked");
 }
 }  // namespace
 
@@ -180,7 +192,7 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
                                                B, H, Hkv, Nq, d, num_pages, max_pages_per_seq,
                                                max_seq_len, causal != 0, scale,
                                                static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return hip_status(e, "fa_fwd_paged");
 }
 
 int fa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
@@ -198,7 +210,7 @@ int fa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_ca
     hipError_t e = kvfa::launch_kv_append(k_new, v_new, k_cache, v_cache, page_table, start_pos,
                                           num_seqs, n_new, Hkv, d, num_pages, max_pages_per_seq,
                                           static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return hip_status(e, "fa_kv_append");
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int Nq) {
@@ -223,7 +235,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
     hipError_t e = kvfa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, Nq, Nk, d,
                                          causal != 0, scale, workspace,
                                          static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return hip_status(e, "fa_bwd");
 }
 
 int fa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,

@@ -499,20 +499,13 @@ hipError_t launch_split(const void* q, const void* kc, const void* vc, const int
                         const float* v_scale, hipStream_t stream) {
     const float scale_log2 = scale * kLog2e;
     // Target: one round of resident work-groups (two for an fp8 cache, whose ranges take
-    // half the time) shared by the (KV head, head group) pairs.
-    static const int per_cu = [] {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<D, GH, FP8>,
-                                                         256, 0) != hipSuccess)
-            n = 1;
-        return std::max(1, n);
-    }();
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return hipErrorInvalidDevice;
+    // half the time) shared by the (KV head, head group) pairs: 256 CUs (MI355X) times the
+    // work-groups a CU holds by the kernels' register use, 3 for 4 heads per group, 2 for
+    // 8, 1 for 16. (Fixed numbers: no runtime query precedes the launch.)
+    constexpr int kCUs = 256;
+    constexpr int per_cu = GH == 4 ? 3 : GH == 8 ? 2 : 1;
     const int groups = Hkv * n_hg;
-    const int target = std::max(1, per_cu * std::max(1, cus) * (FP8 ? 2 : 1) / groups);
+    const int target = std::max(1, per_cu * kCUs * (FP8 ? 2 : 1) / groups);
     // KV heads vary fastest: the work-groups covering one page range are dispatched
     // together, so each physical page (all KV heads of 16 slots, contiguous) is read by
     // concurrently running work-groups.

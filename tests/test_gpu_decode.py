@@ -80,6 +80,24 @@ def test_decode_edge_lengths():
     assert np.all(lse_h[0] == -np.inf)
 
 
+@pytest.mark.parametrize("S,H,Hkv,d,hi,max_seq_len,seed", [
+    (130, 8, 2, 64, 300, 512, 41),        # sequences read in three chunks of 64
+    (200, 4, 1, 128, 40, 131072, 42),     # 248-page ranges, each spanning many sequences
+    (97, 16, 4, 128, 2000, 4096, 43),     # a chunk boundary inside a range
+], ids=lambda x: str(x))
+def test_decode_many_sequences(S, H, Hkv, d, hi, max_seq_len, seed):
+    """More than 64 sequences (the in-kernel page count and prefix sums run over chunks of
+    64 lengths), some of them empty, and ranges cut into many sequence pieces."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, hi + 1, S)
+    lens[rng.integers(0, S, 3)] = 0
+    cfg = inputs.DecodeConfig("many", S, H, Hkv, d, 0, 0, 16, max_seq_len, 1 / math.sqrt(d), seed)
+    inp = inputs.make_decode(cfg, seq_lens=[int(x) for x in lens])
+    o_h, lse_h = _check(inp, f"many sequences S{S}")
+    for s in np.nonzero(lens == 0)[0]:
+        assert np.all(inputs.bf16_bits_to_f32(o_h[s]) == 0.0) and np.all(lse_h[s] == -np.inf)
+
+
 def test_unused_slots_and_table_padding_are_never_read():
     """Slots past a sequence's length hold NaN and unused table entries hold -1: the
     output must be bit-identical to the zero-filled cache's."""
