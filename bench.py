@@ -103,10 +103,12 @@ def cpu_baseline(pinp: inputs.PrefillInputs, budget_s: float = 12.0):
         n_keys = (rows + (c.Nk - c.Nq) + 1) if c.causal else np.full(batch, c.Nk)
         flops += 4.0 * c.d * float(n_keys.sum())
         done_rows += batch
-    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+    rate = flops / t_used
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"{done_rows} random query rows of head 0 of {c.name} (each over its "
-                      f"full causal prefix), fp64 NumPy, {t_used:.1f} s"}
+                      f"full causal prefix), fp64 NumPy, {t_used:.1f} s",
+            "extrapolated_full_config_s": round(c.flops / rate, 1)}
 
 
 def main(argv=None):
@@ -236,11 +238,13 @@ def main(argv=None):
         },
         "legs": {
             "prefill": {"ms_mean": round(float(p_ms.mean()), 4),
+                        "ms_median": round(float(np.median(p_ms)), 4),
                         "ms_p10": round(float(np.percentile(p_ms, 10)), 4),
                         "ms_p90": round(float(np.percentile(p_ms, 90)), 4),
                         "TFLOP/s": round(p_tflops, 2),
                         "frac_of_bf16_peak": round(p_tflops / PEAK_BF16_TFLOPS, 4)},
             "decode": {"ms_mean": round(float(d_ms.mean()), 4),
+                       "ms_median": round(float(np.median(d_ms)), 4),
                        "ms_p10": round(float(np.percentile(d_ms, 10)), 4),
                        "ms_p90": round(float(np.percentile(d_ms, 90)), 4),
                        "GB/s": round(d_gbs, 1),
