@@ -350,17 +350,21 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     // ---- the work-group's range of pages, and the segments in it ----
     // Pages of all sequences end to end (per KV head): sequence s holds [S_s, S_s + P_s).
     // Every wave computes the same plan from the lengths.
-    int P_tot = 0;
+    int P_tot = 0, n_live = 0;
     for (int c0 = 0; c0 < num_seqs; c0 += 64) {
         const int Ls = c0 + lane < num_seqs ? min(max(seq_lens[c0 + lane], 0), max_seq_len) : 0;
         int p = (Ls + kPage - 1) / kPage;
 #pragma unroll
         for (int msk = 1; msk < 64; msk <<= 1) p += __shfl_xor(p, msk, 64);
         P_tot += __builtin_amdgcn_readfirstlane(p);
+        n_live += __builtin_popcountll(__builtin_amdgcn_ballot_w64(Ls > 0));
     }
-    // Work-groups in use: the target, or as many as keep R <= kMaxRangePages (at most the
-    // launched ones, which suffice for the longest possible cache); the rest return.
-    const int n_wg = min((int)gridDim.y, max(wg_target, (P_tot + kMaxRangePages - 1) / kMaxRangePages));
+    // Work-groups in use: the target, at least one per non-empty sequence (many short
+    // sequences then get a range each instead of ranges cut into several short pieces,
+    // each restarting the page pipeline), and as many as keep R <= kMaxRangePages (at most
+    // the launched ones, which suffice for the longest possible cache); the rest return.
+    const int n_wg = min((int)gridDim.y, max(max(wg_target, n_live),
+                                             (P_tot + kMaxRangePages - 1) / kMaxRangePages));
     const int R = max(rmin, (P_tot + n_wg - 1) / n_wg);
     const int g0 = (int)blockIdx.y * R;
     if (g0 >= P_tot) return;  // uniform: nothing left for this work-group
@@ -509,7 +513,7 @@ hipError_t launch_split(const void* q, const void* kc, const void* vc, const int
     // KV heads vary fastest: the work-groups covering one page range are dispatched
     // together, so each physical page (all KV heads of 16 slots, contiguous) is read by
     // concurrently running work-groups.
-    dim3 grid(groups, std::max(target, plan.min_wgs));
+    dim3 grid(groups, std::max(std::max(target, plan.min_wgs), num_seqs));
     hipLaunchKernelGGL((decode_split_kernel<D, GH, FP8>), grid, dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), kc, vc, pt, sl, ws.o_part, ws.lse_part,
                        ws.n_slots, num_seqs, H, Hkv, g, n_hg, num_pages, max_pages, max_seq_len,
