@@ -173,7 +173,7 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  * Everything else (q, o, lse, page_table, seq_lens, workspace and its size, errors,
  * device-side behaviour) is as for fa_decode_paged. The result is the attention of the
  * dequantised cache: bytes are converted exactly, scores and the softmax are fp32 and
- * the K scale is folded into the softmax scale, the V scale into each split's output.
+ * the K scale is folded into the softmax scale, the V scale into each partial result.
  * k_scale or v_scale NULL or misaligned: FA_ERR_INVALID.
  */
 int fa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,

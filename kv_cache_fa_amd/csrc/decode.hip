@@ -5,8 +5,8 @@
 // (its own K/V already appended); the cache lives in fixed-size pages; under GQA
 // several query heads share one K/V head. The softmax over the cached keys uses the
 // running max / running sum merge of page "Donanıma Duyarlı Algoritma Tasarımı:
-// FlashAttention", "Online Softmax Prensibi" steps 1-5, both inside a split (page by
-// page) and across splits (the combine kernel merges (O_k, lse_k) pairs, the same
+// FlashAttention", "Online Softmax Prensibi" steps 1-5, both inside a segment (page by
+// page) and across segments (the combine kernel merges (O_k, lse_k) pairs, the same
 // algebra expressed through one log-sum-exp per part).
 //
 // gfx950 mapping (this design):
@@ -68,7 +68,7 @@ DecodePlan decode_plan(int num_seqs, int max_seq_len) {
 // FP8 = true: the cache holds e4m3 bytes with one scale per KV head for K and one for V
 // (dequantised value = byte value x scale). K bytes are converted exactly to bf16 for the
 // MFMA and V bytes to fp32 for the P.V FMAs; the K scale is folded into the softmax
-// scale and the V scale is applied to the split's output, so the arithmetic is that of
+// scale and the V scale is applied to each partial result, so the arithmetic is that of
 // the dequantised cache. Each cached token costs half the bytes of the bf16 cache.
 template <int D, int GH, bool FP8>
 __global__ __launch_bounds__(256) void decode_split_kernel(
@@ -398,9 +398,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 
 // Merge the slots of each (sequence, head): LSE = log2 sum_k 2^lse_k (relative to the
 // largest), O = sum_k 2^(lse_k - LSE) O_k. One wave per (sequence, head), kCombineHeads
-// heads per work-group. The split statistics are spread over the lanes (one split per
+// heads per work-group. The slot statistics are spread over the lanes (one slot per
 // lane, wave reductions for the max and the sum); each lane then owns D/64 output dims and
-// walks the splits with eight partial rows in flight, the weights broadcast from the lane
+// walks the slots with eight partial rows in flight, the weights broadcast from the lane
 // that holds them.
 constexpr int kCombineHeads = 4;
 template <int D>
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(64 * kCombineHeads) void decode_combine_kernel(
     for (int k = lane; k < ns; k += 64) m = fmaxf(m, lp[k]);
 #pragma unroll
     for (int msk = 1; msk < 64; msk <<= 1) m = fmaxf(m, shfl_xor(m, msk));
-    const float M = m;  // -inf: no split holds a token (L = 0)
+    const float M = m;  // -inf: no slot holds a token (L = 0)
 
     float out[PER];
 #pragma unroll
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(64 * kCombineHeads) void decode_combine_kernel(
     float wsum = 0.f;
     if (M != -INFINITY) {
         for (int kb = 0; kb < ns; kb += 64) {
-            // weight of split kb + lane (0 past the last split)
+            // weight of slot kb + lane (0 past the last slot)
             const float fl = kb + lane < ns ? fast_exp2(lp[kb + lane] - M) : 0.f;
             wsum += fl;
             const int cnt = min(64, ns - kb);

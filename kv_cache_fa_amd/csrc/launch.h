@@ -44,7 +44,9 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                            void* workspace, hipStream_t stream);
 
-// Decode split plan: tokens per split-K work-group, and the workspace it implies.
+// Decode range plan: the fewest cached tokens a split-K work-group's range holds, the
+// work-groups per (KV head, head group) the longest possible cache needs, and the
+// workspace the plan implies.
 int decode_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size);
 int decode_min_work_groups(int num_seqs, int max_seq_len);
 size_t decode_workspace_bytes(int num_seqs, int H, int Hkv, int d, int max_seq_len,
