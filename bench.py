@@ -288,6 +288,22 @@ def main(argv=None):
             "B": gcfg.B, "H": gcfg.H, "Hkv": gcfg.Hkv, "N": gcfg.Nq, "d": gcfg.d,
             "ms_mean": round(g_ms, 4), "TFLOP/s": round(g_tf, 2),
             "frac_of_bf16_peak": round(g_tf / PEAK_BF16_TFLOPS, 4)}
+        # The small causal case (B2 H8 N1024 d64): a few microseconds, so launch-bound;
+        # reported, not a target.
+        scfg = inputs.PREFILL_CONFIGS["bf16_causal"]
+        log("[bench] extra: bf16_causal prefill")
+        sinp = inputs.make_prefill(scfg)
+        sq, sk, sv = to_dev(sinp.q), to_dev(sinp.k), to_dev(sinp.v)
+        so = torch.empty_like(sq)
+        slse = torch.empty((scfg.B, scfg.H, scfg.Nq), dtype=torch.float32, device=dev)
+        s_ms = timed(lambda: _lib.fa_fwd(sq, sk, sv, so, slse, causal=True, scale=scfg.scale,
+                                         stream=stream), n=100)
+        s_tf = scfg.flops / (s_ms * 1e-3) / 1e12
+        out["legs"]["prefill_small_causal"] = {
+            "B": scfg.B, "H": scfg.H, "Hkv": scfg.Hkv, "N": scfg.Nq, "d": scfg.d,
+            "ms_mean": round(s_ms, 4), "TFLOP/s": round(s_tf, 2),
+            "frac_of_bf16_peak": round(s_tf / PEAK_BF16_TFLOPS, 4)}
+        del sq, sk, sv, so, slse
         # The same workload through the FlashAttention-1 two-pass path (statistics pass +
         # output pass); TFLOP/s counts the algorithmic flops, not the recomputed Q.K^T.
         log("[bench] extra: gqa_causal two-pass")
