@@ -107,6 +107,16 @@ def test_fp32_shapes(shape):
     _dense_check(inp, f"fp32 {shape}")
 
 
+def test_bf16_largest_head_slice():
+    """The largest K/V slice one head may have (Nk * d * 2 bytes just under 2^31, the
+    32-bit buffer-offset limit of the ABI): 8388544 keys, d = 128, 100 ragged query rows,
+    non-causal; four rows checked against the oracle over all keys."""
+    Nk = (1 << 23) - 64
+    assert Nk * 128 * 2 < 1 << 31
+    inp = inputs.custom_prefill(1, 1, 1, 100, Nk, 128, False, seed=77)
+    _sampled_check(inp, {(0, 0): np.array([0, 37, 63, 99])}, "largest head slice")
+
+
 def test_bf16_scale_not_default():
     inp = inputs.custom_prefill(1, 2, 2, 300, 300, 128, True, "bf16", scale=0.3, seed=9)
     _dense_check(inp, "bf16 scale=0.3")
