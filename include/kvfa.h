@@ -188,7 +188,8 @@ int fa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
  * The cached pages of all sequences, end to end, are cut into equal ranges of at least
  * this many tokens, one per work-group; a sequence is thereby cut into at most
  * ceil(max_seq_len / split) + 1 pieces, and the workspace holds that many partial results
- * per head (plus one int32 per sequence). */
+ * per head, plus two int32 per sequence and two more (slot counts and, for more than 64
+ * sequences, each sequence's first page, computed by a small planning kernel). */
 int fa_decode_paged_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size);
 
 /*

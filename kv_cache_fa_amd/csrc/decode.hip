@@ -75,7 +75,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kcache,
     const void* __restrict__ vcache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
-    float* __restrict__ lse_part, int* __restrict__ n_slots, int num_seqs, int H, int Hkv,
+    float* __restrict__ lse_part, int* __restrict__ n_slots, const int* __restrict__ plan,
+    int num_seqs, int H, int Hkv,
     int g, int n_hg, int num_pages, int max_pages, int max_seq_len, int rmin, int max_slots,
     int wg_target, float scale_log2_in, const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
     constexpr int ES = FP8 ? 1 : 2;    // bytes per cached element
@@ -350,14 +351,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     // ---- the work-group's range of pages, and the segments in it ----
     // Pages of all sequences end to end (per KV head): sequence s holds [S_s, S_s + P_s).
     // Every wave computes the same plan from the lengths.
-    int P_tot = 0, n_live = 0;
-    for (int c0 = 0; c0 < num_seqs; c0 += 64) {
-        const int Ls = c0 + lane < num_seqs ? min(max(seq_lens[c0 + lane], 0), max_seq_len) : 0;
+    // Up to 64 sequences: their lengths are one load per lane and a wave reduction. More:
+    // the totals and each sequence's first page come from the plan kernel (decode_plan_kernel),
+    // so no work-group reads every length.
+    int P_tot, n_live;
+    if (plan != nullptr) {
+        P_tot = plan[num_seqs];
+        n_live = plan[num_seqs + 1];
+    } else {
+        const int Ls = lane < num_seqs ? min(max(seq_lens[lane], 0), max_seq_len) : 0;
         int p = (Ls + kPage - 1) / kPage;
 #pragma unroll
         for (int msk = 1; msk < 64; msk <<= 1) p += __shfl_xor(p, msk, 64);
-        P_tot += __builtin_amdgcn_readfirstlane(p);
-        n_live += __builtin_popcountll(__builtin_amdgcn_ballot_w64(Ls > 0));
+        P_tot = __builtin_amdgcn_readfirstlane(p);
+        n_live = __builtin_popcountll(__builtin_amdgcn_ballot_w64(Ls > 0));
     }
     // Work-groups in use: the target, at least one per non-empty sequence (many short
     // sequences then get a range each instead of ranges cut into several short pieces,
@@ -369,8 +376,26 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const int g0 = (int)blockIdx.y * R;
     if (g0 >= P_tot) return;  // uniform: nothing left for this work-group
     const int g1 = min(g0 + R, P_tot);
-    int base = 0;  // pages of the sequences before the current 64
-    for (int c0 = 0; c0 < num_seqs && base < g1; c0 += 64) {
+    int c_first = 0, base = 0;  // first sequence to look at, pages of those before it
+    if (plan != nullptr) {
+        // The sequence holding page g0: the last s with plan[s] <= g0 (an empty sequence
+        // starts where its successor does and loses to it), by a 64-way search; plan[lo]
+        // <= g0 holds throughout and the answer stays in [lo, hi).
+        int lo = 0, hi = num_seqs;
+        while (hi - lo > 64) {
+            const int stride = (hi - lo + 63) / 64;
+            const int pos = lo + lane * stride;
+            const unsigned long long m =
+                __builtin_amdgcn_ballot_w64(pos < hi && plan[pos] <= g0);
+            lo += (63 - __builtin_clzll(m)) * stride;
+            hi = min(hi, lo + stride);
+        }
+        const unsigned long long m =
+            __builtin_amdgcn_ballot_w64(lo + lane < hi && plan[lo + lane] <= g0);
+        c_first = lo + (63 - __builtin_clzll(m));
+        base = plan[c_first];
+    }
+    for (int c0 = c_first; c0 < num_seqs && base < g1; c0 += 64) {
         const int Ls = c0 + lane < num_seqs ? min(max(seq_lens[c0 + lane], 0), max_seq_len) : 0;
         const int Ps = (Ls + kPage - 1) / kPage;
         int x = Ps;  // inclusive prefix sum over the lanes
@@ -393,6 +418,46 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
             segment(c0 + ln, __builtin_amdgcn_readlane(Ls, ln), a, b - a, slot);
         }
         base += __builtin_amdgcn_readlane(x, 63);
+    }
+}
+
+// Plan for more than 64 sequences: plan[s] = pages of the sequences before s (exclusive
+// prefix sum of ceil(len / 16)), plan[num_seqs] = all pages, plan[num_seqs + 1] = the
+// non-empty sequences. One work-group of 1024 threads walks the lengths 1024 at a time.
+__global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __restrict__ seq_lens,
+                                                           int num_seqs, int max_seq_len,
+                                                           int* __restrict__ plan) {
+    __shared__ int wave_pages[16], wave_live[16];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int carry = 0, live = 0;
+    for (int c0 = 0; c0 < num_seqs; c0 += 1024) {
+        const int s = c0 + tid;
+        const int L = s < num_seqs ? min(max(seq_lens[s], 0), max_seq_len) : 0;
+        const int P = (L + kPage - 1) / kPage;
+        int x = P;  // inclusive prefix sum over the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        const unsigned long long live_mask = __builtin_amdgcn_ballot_w64(L > 0);  // all lanes vote
+        if (lane == 63) wave_pages[w] = x;
+        if (lane == 0) wave_live[w] = __builtin_popcountll(live_mask);
+        __syncthreads();
+        int before = 0, total = 0, nl = 0;
+        for (int i = 0; i < 16; ++i) {
+            before += i < w ? wave_pages[i] : 0;
+            total += wave_pages[i];
+            nl += wave_live[i];
+        }
+        if (s < num_seqs) plan[s] = carry + before + x - P;
+        carry += total;
+        live += nl;
+        __syncthreads();  // the sums are rewritten by the next 1024
+    }
+    if (tid == 0) {
+        plan[num_seqs] = carry;
+        plan[num_seqs + 1] = live;
     }
 }
 
@@ -482,17 +547,19 @@ __global__ __launch_bounds__(64 * kCombineHeads) void decode_combine_kernel(
 }
 
 // Workspace: o_part [num_seqs, H, max_slots, D] fp32, lse_part [num_seqs, H, max_slots]
-// fp32, n_slots [num_seqs] int32.
+// fp32, n_slots [num_seqs] int32, plan [num_seqs + 2] int32.
 struct DecodeWorkspace {
     float* o_part;
     float* lse_part;
     int* n_slots;
+    int* plan;
 };
 DecodeWorkspace decode_workspace(void* ws, int num_seqs, int H, int d, int max_slots) {
     const size_t rows = (size_t)num_seqs * H * max_slots;
     float* o_part = static_cast<float*>(ws);
     float* lse_part = o_part + rows * d;
-    return {o_part, lse_part, reinterpret_cast<int*>(lse_part + rows)};
+    int* n_slots = reinterpret_cast<int*>(lse_part + rows);
+    return {o_part, lse_part, n_slots, n_slots + num_seqs};
 }
 
 template <int D, int GH, bool FP8>
@@ -516,7 +583,8 @@ hipError_t launch_split(const void* q, const void* kc, const void* vc, const int
     dim3 grid(groups, std::max(std::max(target, plan.min_wgs), num_seqs));
     hipLaunchKernelGGL((decode_split_kernel<D, GH, FP8>), grid, dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), kc, vc, pt, sl, ws.o_part, ws.lse_part,
-                       ws.n_slots, num_seqs, H, Hkv, g, n_hg, num_pages, max_pages, max_seq_len,
+                       ws.n_slots, num_seqs > 64 ? ws.plan : nullptr, num_seqs, H, Hkv, g, n_hg,
+                       num_pages, max_pages, max_seq_len,
                        plan.rmin, plan.max_slots, target, scale_log2, k_scale, v_scale);
     return hipGetLastError();
 }
@@ -556,7 +624,7 @@ size_t decode_workspace_bytes(int num_seqs, int H, int Hkv, int d, int max_seq_l
     const DecodePlan plan = decode_plan(num_seqs, max_seq_len);
     const size_t rows = (size_t)num_seqs * H * plan.max_slots;
     return rows * (size_t)d * sizeof(float) + rows * sizeof(float) +
-           (size_t)num_seqs * sizeof(int);
+           (size_t)num_seqs * sizeof(int) + ((size_t)num_seqs + 2) * sizeof(int);
 }
 
 hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -573,6 +641,12 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
     const DecodeWorkspace ws = decode_workspace(workspace, num_seqs, H, d, plan.max_slots);
 
     hipError_t e;
+    if (num_seqs > 64) {
+        hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, seq_lens,
+                           num_seqs, max_seq_len, ws.plan);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     if (d == 128)
         e = fp8 ? launch_split_d<128, true>(GH, q, k_cache, v_cache, page_table, seq_lens, ws,
                                             plan, num_seqs, H, Hkv, g, n_hg, num_pages,

@@ -200,7 +200,8 @@ def test_workspace_size(lib):
     T = lib.fa_decode_paged_split_tokens(64, 8, 8192, 16)
     assert T == 16 * 16
     slots = -(-8192 // T) + 1  # segments a sequence can be cut into
-    assert f(64, 32, 8, 128, 8192, 16) == 64 * 32 * slots * (128 + 1) * 4 + 64 * 4
+    # partial results, then per sequence its slot count and (plan) its first page, + 2 totals
+    assert f(64, 32, 8, 128, 8192, 16) == 64 * 32 * slots * (128 + 1) * 4 + 64 * 4 + 66 * 4
     assert lib.fa_decode_paged_split_tokens(1, 1, 100, 16) == 4 * 16
     assert lib.fa_decode_paged_split_tokens(1, 1, 131072, 16) == 248 * 16
     assert lib.fa_decode_paged_split_tokens(1, 1, 1 << 30, 16) == 248 * 16
