@@ -188,8 +188,9 @@ int fa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
  * The cached pages of all sequences, end to end, are cut into equal ranges of at least
  * this many tokens, one per work-group; a sequence is thereby cut into at most
  * ceil(max_seq_len / split) + 1 pieces, and the workspace holds that many partial results
- * per head, plus two int32 per sequence and two more (slot counts and, for more than 64
- * sequences, each sequence's first page, computed by a small planning kernel). */
+ * per head, plus one int32 per sequence (its slot count) and a plan of 4 + 2 x max(1536,
+ * ceil(num_seqs x max_pages / 248), num_seqs) int32 (for more than 64 sequences a small
+ * planning kernel writes where each work-group's range starts). */
 int fa_decode_paged_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size);
 
 /*

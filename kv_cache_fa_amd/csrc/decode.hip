@@ -351,50 +351,35 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     // ---- the work-group's range of pages, and the segments in it ----
     // Pages of all sequences end to end (per KV head): sequence s holds [S_s, S_s + P_s).
     // Every wave computes the same plan from the lengths.
-    // Up to 64 sequences: their lengths are one load per lane and a wave reduction. More:
-    // the totals and each sequence's first page come from the plan kernel (decode_plan_kernel),
-    // so no work-group reads every length.
-    int P_tot, n_live;
+    // Work-groups in use: the target, at least one per non-empty sequence (many short
+    // sequences then get a range each instead of ranges cut into several short pieces,
+    // each restarting the page pipeline), and as many as keep R <= kMaxRangePages (at most
+    // the launched ones, which suffice for the longest possible cache); the rest return.
+    // Up to 64 sequences every work-group works this out from the lengths (one load per
+    // lane); beyond, decode_plan_kernel has done it once and also recorded where each
+    // work-group's range starts, so no work-group reads every length.
+    int P_tot, n_wg, R, c_first = 0, base = 0;  // base: pages of the sequences before c_first
     if (plan != nullptr) {
-        P_tot = plan[num_seqs];
-        n_live = plan[num_seqs + 1];
+        P_tot = plan[0];
+        n_wg = plan[1];
+        R = plan[2];
+        if ((int)blockIdx.y >= n_wg || (int)blockIdx.y * R >= P_tot) return;  // uniform
+        c_first = plan[4 + 2 * blockIdx.y];
+        base = plan[5 + 2 * blockIdx.y];
     } else {
         const int Ls = lane < num_seqs ? min(max(seq_lens[lane], 0), max_seq_len) : 0;
         int p = (Ls + kPage - 1) / kPage;
 #pragma unroll
         for (int msk = 1; msk < 64; msk <<= 1) p += __shfl_xor(p, msk, 64);
         P_tot = __builtin_amdgcn_readfirstlane(p);
-        n_live = __builtin_popcountll(__builtin_amdgcn_ballot_w64(Ls > 0));
+        const int n_live = __builtin_popcountll(__builtin_amdgcn_ballot_w64(Ls > 0));
+        n_wg = min((int)gridDim.y,
+                   max(max(wg_target, n_live), (P_tot + kMaxRangePages - 1) / kMaxRangePages));
+        R = max(rmin, (P_tot + n_wg - 1) / n_wg);
+        if ((int)blockIdx.y * R >= P_tot) return;  // uniform: nothing left for this one
     }
-    // Work-groups in use: the target, at least one per non-empty sequence (many short
-    // sequences then get a range each instead of ranges cut into several short pieces,
-    // each restarting the page pipeline), and as many as keep R <= kMaxRangePages (at most
-    // the launched ones, which suffice for the longest possible cache); the rest return.
-    const int n_wg = min((int)gridDim.y, max(max(wg_target, n_live),
-                                             (P_tot + kMaxRangePages - 1) / kMaxRangePages));
-    const int R = max(rmin, (P_tot + n_wg - 1) / n_wg);
     const int g0 = (int)blockIdx.y * R;
-    if (g0 >= P_tot) return;  // uniform: nothing left for this work-group
     const int g1 = min(g0 + R, P_tot);
-    int c_first = 0, base = 0;  // first sequence to look at, pages of those before it
-    if (plan != nullptr) {
-        // The sequence holding page g0: the last s with plan[s] <= g0 (an empty sequence
-        // starts where its successor does and loses to it), by a 64-way search; plan[lo]
-        // <= g0 holds throughout and the answer stays in [lo, hi).
-        int lo = 0, hi = num_seqs;
-        while (hi - lo > 64) {
-            const int stride = (hi - lo + 63) / 64;
-            const int pos = lo + lane * stride;
-            const unsigned long long m =
-                __builtin_amdgcn_ballot_w64(pos < hi && plan[pos] <= g0);
-            lo += (63 - __builtin_clzll(m)) * stride;
-            hi = min(hi, lo + stride);
-        }
-        const unsigned long long m =
-            __builtin_amdgcn_ballot_w64(lo + lane < hi && plan[lo + lane] <= g0);
-        c_first = lo + (63 - __builtin_clzll(m));
-        base = plan[c_first];
-    }
     for (int c0 = c_first; c0 < num_seqs && base < g1; c0 += 64) {
         const int Ls = c0 + lane < num_seqs ? min(max(seq_lens[c0 + lane], 0), max_seq_len) : 0;
         const int Ps = (Ls + kPage - 1) / kPage;
@@ -421,43 +406,73 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     }
 }
 
-// Plan for more than 64 sequences: plan[s] = pages of the sequences before s (exclusive
-// prefix sum of ceil(len / 16)), plan[num_seqs] = all pages, plan[num_seqs + 1] = the
-// non-empty sequences. One work-group of 1024 threads walks the lengths 1024 at a time.
+// Plan for more than 64 sequences (the split kernel's work-group rule, worked out once):
+// plan[0] = all pages (per KV head), plan[1] = work-groups in use, plan[2] = R (pages per
+// range); for work-group j < plan[1] whose range starts before the end, plan[4 + 2j] = the
+// sequence holding its first page j R and plan[5 + 2j] = that sequence's first page.
+// Sequence s, holding pages [S_s, S_s + P_s), is that sequence for every j with
+// S_s <= j R < S_s + P_s, so a second pass over the lengths fills the table with no search.
+// One work-group of 1024 threads walks the lengths 1024 at a time.
+__device__ __forceinline__ void plan_prefix(const int32_t* __restrict__ seq_lens, int num_seqs,
+                                            int max_seq_len, int c0, int carry, int* wave_sums,
+                                            int& L, int& P, int& S, int& chunk_total,
+                                            int& chunk_live) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int s = c0 + tid;
+    L = s < num_seqs ? min(max(seq_lens[s], 0), max_seq_len) : 0;
+    P = (L + kPage - 1) / kPage;
+    int x = P;  // inclusive prefix sum over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    const unsigned long long live_mask = __builtin_amdgcn_ballot_w64(L > 0);  // all lanes vote
+    if (lane == 63) wave_sums[w] = x;
+    if (lane == 0) wave_sums[16 + w] = __builtin_popcountll(live_mask);
+    __syncthreads();
+    int before = 0;
+    chunk_total = 0;
+    chunk_live = 0;
+    for (int i = 0; i < 16; ++i) {
+        before += i < w ? wave_sums[i] : 0;
+        chunk_total += wave_sums[i];
+        chunk_live += wave_sums[16 + i];
+    }
+    S = carry + before + x - P;
+    __syncthreads();  // the sums are rewritten by the next 1024
+}
+
 __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __restrict__ seq_lens,
                                                            int num_seqs, int max_seq_len,
-                                                           int* __restrict__ plan) {
-    __shared__ int wave_pages[16], wave_live[16];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    int carry = 0, live = 0;
+                                                           int wg_target, int wg_launched,
+                                                           int rmin, int* __restrict__ plan) {
+    __shared__ int wave_sums[32];
+    int L, P, S, total, live_c;
+    int P_tot = 0, live = 0;
     for (int c0 = 0; c0 < num_seqs; c0 += 1024) {
-        const int s = c0 + tid;
-        const int L = s < num_seqs ? min(max(seq_lens[s], 0), max_seq_len) : 0;
-        const int P = (L + kPage - 1) / kPage;
-        int x = P;  // inclusive prefix sum over the wave
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(x, o, 64);
-            if (lane >= o) x += y;
-        }
-        const unsigned long long live_mask = __builtin_amdgcn_ballot_w64(L > 0);  // all lanes vote
-        if (lane == 63) wave_pages[w] = x;
-        if (lane == 0) wave_live[w] = __builtin_popcountll(live_mask);
-        __syncthreads();
-        int before = 0, total = 0, nl = 0;
-        for (int i = 0; i < 16; ++i) {
-            before += i < w ? wave_pages[i] : 0;
-            total += wave_pages[i];
-            nl += wave_live[i];
-        }
-        if (s < num_seqs) plan[s] = carry + before + x - P;
-        carry += total;
-        live += nl;
-        __syncthreads();  // the sums are rewritten by the next 1024
+        plan_prefix(seq_lens, num_seqs, max_seq_len, c0, P_tot, wave_sums, L, P, S, total, live_c);
+        P_tot += total;
+        live += live_c;
     }
-    if (tid == 0) {
-        plan[num_seqs] = carry;
-        plan[num_seqs + 1] = live;
+    const int n_wg = min(wg_launched,
+                         max(max(wg_target, live), (P_tot + kMaxRangePages - 1) / kMaxRangePages));
+    const int R = max(rmin, (P_tot + n_wg - 1) / n_wg);
+    if (threadIdx.x == 0) {
+        plan[0] = P_tot;
+        plan[1] = n_wg;
+        plan[2] = R;
+        plan[3] = live;
+    }
+    int carry = 0;
+    for (int c0 = 0; c0 < num_seqs; c0 += 1024) {
+        plan_prefix(seq_lens, num_seqs, max_seq_len, c0, carry, wave_sums, L, P, S, total, live_c);
+        carry += total;
+        if (P > 0)
+            for (int j = (S + R - 1) / R; j * R < S + P && j < n_wg; ++j) {
+                plan[4 + 2 * j] = c0 + (int)threadIdx.x;
+                plan[5 + 2 * j] = S;
+            }
     }
 }
 
@@ -547,7 +562,7 @@ __global__ __launch_bounds__(64 * kCombineHeads) void decode_combine_kernel(
 }
 
 // Workspace: o_part [num_seqs, H, max_slots, D] fp32, lse_part [num_seqs, H, max_slots]
-// fp32, n_slots [num_seqs] int32, plan [num_seqs + 2] int32.
+// fp32, n_slots [num_seqs] int32, plan [4 + 2 x the launched work-groups] int32.
 struct DecodeWorkspace {
     float* o_part;
     float* lse_part;
@@ -562,25 +577,32 @@ DecodeWorkspace decode_workspace(void* ws, int num_seqs, int H, int d, int max_s
     return {o_part, lse_part, n_slots, n_slots + num_seqs};
 }
 
+// Work-groups aimed at: one round of resident ones (two for an fp8 cache, whose ranges take
+// half the time) shared by the (KV head, head group) pairs: 256 CUs (MI355X) times the
+// work-groups a CU holds by the kernels' register use, 3 for 4 heads per group, 2 for 8,
+// 1 for 16. (Fixed numbers: no runtime query precedes the launch.)
+constexpr int kCUs = 256;
+int decode_target(int GH, bool fp8, int groups) {
+    const int per_cu = GH == 4 ? 3 : GH == 8 ? 2 : 1;
+    return std::max(1, per_cu * kCUs * (fp8 ? 2 : 1) / groups);
+}
+// The most work-groups per (KV head, head group) a launch can have, for any head count or
+// cache type: sizes the plan in the workspace.
+int decode_max_rows(const DecodePlan& plan, int num_seqs) {
+    return std::max(std::max(3 * kCUs * 2, plan.min_wgs), num_seqs);
+}
+
 template <int D, int GH, bool FP8>
 hipError_t launch_split(const void* q, const void* kc, const void* vc, const int32_t* pt,
                         const int32_t* sl, const DecodeWorkspace& ws, const DecodePlan& plan,
-                        int num_seqs, int H, int Hkv, int g, int n_hg, int num_pages,
-                        int max_pages, int max_seq_len, float scale, const float* k_scale,
-                        const float* v_scale, hipStream_t stream) {
+                        int target, int rows, int num_seqs, int H, int Hkv, int g, int n_hg,
+                        int num_pages, int max_pages, int max_seq_len, float scale,
+                        const float* k_scale, const float* v_scale, hipStream_t stream) {
     const float scale_log2 = scale * kLog2e;
-    // Target: one round of resident work-groups (two for an fp8 cache, whose ranges take
-    // half the time) shared by the (KV head, head group) pairs: 256 CUs (MI355X) times the
-    // work-groups a CU holds by the kernels' register use, 3 for 4 heads per group, 2 for
-    // 8, 1 for 16. (Fixed numbers: no runtime query precedes the launch.)
-    constexpr int kCUs = 256;
-    constexpr int per_cu = GH == 4 ? 3 : GH == 8 ? 2 : 1;
-    const int groups = Hkv * n_hg;
-    const int target = std::max(1, per_cu * kCUs * (FP8 ? 2 : 1) / groups);
     // KV heads vary fastest: the work-groups covering one page range are dispatched
     // together, so each physical page (all KV heads of 16 slots, contiguous) is read by
     // concurrently running work-groups.
-    dim3 grid(groups, std::max(std::max(target, plan.min_wgs), num_seqs));
+    dim3 grid(Hkv * n_hg, rows);
     hipLaunchKernelGGL((decode_split_kernel<D, GH, FP8>), grid, dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), kc, vc, pt, sl, ws.o_part, ws.lse_part,
                        ws.n_slots, num_seqs > 64 ? ws.plan : nullptr, num_seqs, H, Hkv, g, n_hg,
@@ -592,16 +614,17 @@ hipError_t launch_split(const void* q, const void* kc, const void* vc, const int
 template <int D, bool FP8>
 hipError_t launch_split_d(int GH, const void* q, const void* kc, const void* vc,
                           const int32_t* pt, const int32_t* sl, const DecodeWorkspace& ws,
-                          const DecodePlan& plan, int num_seqs, int H, int Hkv, int g, int n_hg,
-                          int num_pages, int max_pages, int max_seq_len, float scale,
-                          const float* ks, const float* vs, hipStream_t stream) {
+                          const DecodePlan& plan, int target, int rows, int num_seqs, int H,
+                          int Hkv, int g, int n_hg, int num_pages, int max_pages,
+                          int max_seq_len, float scale, const float* ks, const float* vs,
+                          hipStream_t stream) {
     if (GH == 4)
-        return launch_split<D, 4, FP8>(q, kc, vc, pt, sl, ws, plan, num_seqs, H, Hkv, g, n_hg,
+        return launch_split<D, 4, FP8>(q, kc, vc, pt, sl, ws, plan, target, rows, num_seqs, H, Hkv, g, n_hg,
                                        num_pages, max_pages, max_seq_len, scale, ks, vs, stream);
     if (GH == 8)
-        return launch_split<D, 8, FP8>(q, kc, vc, pt, sl, ws, plan, num_seqs, H, Hkv, g, n_hg,
+        return launch_split<D, 8, FP8>(q, kc, vc, pt, sl, ws, plan, target, rows, num_seqs, H, Hkv, g, n_hg,
                                        num_pages, max_pages, max_seq_len, scale, ks, vs, stream);
-    return launch_split<D, 16, FP8>(q, kc, vc, pt, sl, ws, plan, num_seqs, H, Hkv, g, n_hg,
+    return launch_split<D, 16, FP8>(q, kc, vc, pt, sl, ws, plan, target, rows, num_seqs, H, Hkv, g, n_hg,
                                     num_pages, max_pages, max_seq_len, scale, ks, vs, stream);
 }
 
@@ -624,7 +647,8 @@ size_t decode_workspace_bytes(int num_seqs, int H, int Hkv, int d, int max_seq_l
     const DecodePlan plan = decode_plan(num_seqs, max_seq_len);
     const size_t rows = (size_t)num_seqs * H * plan.max_slots;
     return rows * (size_t)d * sizeof(float) + rows * sizeof(float) +
-           (size_t)num_seqs * sizeof(int) + ((size_t)num_seqs + 2) * sizeof(int);
+           (size_t)num_seqs * sizeof(int) +
+           (4 + 2 * (size_t)decode_max_rows(plan, num_seqs)) * sizeof(int);
 }
 
 hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -640,29 +664,32 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
     const DecodePlan plan = decode_plan(num_seqs, max_seq_len);
     const DecodeWorkspace ws = decode_workspace(workspace, num_seqs, H, d, plan.max_slots);
 
+    const int target = decode_target(GH, fp8, Hkv * n_hg);
+    const int rows = std::max(std::max(target, plan.min_wgs), num_seqs);  // <= decode_max_rows
+
     hipError_t e;
     if (num_seqs > 64) {
         hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, seq_lens,
-                           num_seqs, max_seq_len, ws.plan);
+                           num_seqs, max_seq_len, target, rows, plan.rmin, ws.plan);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (d == 128)
         e = fp8 ? launch_split_d<128, true>(GH, q, k_cache, v_cache, page_table, seq_lens, ws,
-                                            plan, num_seqs, H, Hkv, g, n_hg, num_pages,
+                                            plan, target, rows, num_seqs, H, Hkv, g, n_hg, num_pages,
                                             max_pages_per_seq, max_seq_len, scale, k_scale,
                                             v_scale, stream)
                 : launch_split_d<128, false>(GH, q, k_cache, v_cache, page_table, seq_lens, ws,
-                                             plan, num_seqs, H, Hkv, g, n_hg, num_pages,
+                                             plan, target, rows, num_seqs, H, Hkv, g, n_hg, num_pages,
                                              max_pages_per_seq, max_seq_len, scale, nullptr,
                                              nullptr, stream);
     else
         e = fp8 ? launch_split_d<64, true>(GH, q, k_cache, v_cache, page_table, seq_lens, ws,
-                                           plan, num_seqs, H, Hkv, g, n_hg, num_pages,
+                                           plan, target, rows, num_seqs, H, Hkv, g, n_hg, num_pages,
                                            max_pages_per_seq, max_seq_len, scale, k_scale,
                                            v_scale, stream)
                 : launch_split_d<64, false>(GH, q, k_cache, v_cache, page_table, seq_lens, ws,
-                                            plan, num_seqs, H, Hkv, g, n_hg, num_pages,
+                                            plan, target, rows, num_seqs, H, Hkv, g, n_hg, num_pages,
                                             max_pages_per_seq, max_seq_len, scale, nullptr,
                                             nullptr, stream);
     if (e != hipSuccess) return e;

@@ -200,8 +200,11 @@ def test_workspace_size(lib):
     T = lib.fa_decode_paged_split_tokens(64, 8, 8192, 16)
     assert T == 16 * 16
     slots = -(-8192 // T) + 1  # segments a sequence can be cut into
-    # partial results, then per sequence its slot count and (plan) its first page, + 2 totals
-    assert f(64, 32, 8, 128, 8192, 16) == 64 * 32 * slots * (128 + 1) * 4 + 64 * 4 + 66 * 4
+    # partial results, per sequence its slot count, then the plan: 4 totals and 2 ints per
+    # work-group row (at most max(1536, work-groups the longest cache needs, sequences))
+    rows = max(1536, -(-(64 * 512) // 248), 64)
+    assert f(64, 32, 8, 128, 8192, 16) == (64 * 32 * slots * (128 + 1) * 4 + 64 * 4
+                                           + (4 + 2 * rows) * 4)
     assert lib.fa_decode_paged_split_tokens(1, 1, 100, 16) == 4 * 16
     assert lib.fa_decode_paged_split_tokens(1, 1, 131072, 16) == 248 * 16
     assert lib.fa_decode_paged_split_tokens(1, 1, 1 << 30, 16) == 248 * 16
