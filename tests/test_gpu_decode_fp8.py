@@ -86,6 +86,18 @@ def test_fp8_decode_long_ranges():
     _check(inputs.quantize_decode_fp8(base), "fp8 long ranges")
 
 
+def test_fp8_decode_many_sequences():
+    """150 sequences on an e4m3 cache (the planning kernel's path), some empty."""
+    rng = np.random.default_rng(44)
+    lens = rng.integers(0, 700, 150)
+    lens[rng.integers(0, 150, 4)] = 0
+    cfg = inputs.DecodeConfig("many", 150, 8, 2, 128, 0, 0, 16, 1024, 1 / math.sqrt(128), 44)
+    base = inputs.make_decode(cfg, seq_lens=[int(x) for x in lens])
+    o_h, lse_h = _check(inputs.quantize_decode_fp8(base), "fp8 many sequences")
+    for s in np.nonzero(lens == 0)[0]:
+        assert np.all(inputs.bf16_bits_to_f32(o_h[s]) == 0.0) and np.all(lse_h[s] == -np.inf)
+
+
 def test_fp8_edge_lengths_and_nan_slots():
     """Empty sequence, page boundaries; unused slots hold e4m3 NaN bytes and the table is
     padded with -1: the output must equal the zero-filled cache's bit for bit."""
