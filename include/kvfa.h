@@ -143,10 +143,13 @@ int fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float*
  *              owned by the caller; its contents on entry do not matter.
  * Work is split over the KV length (split-K: every work-group reads an equal range of
  * the cached pages, read from seq_lens on the device); the partial results are merged by
- * their log-sum-exps in a second kernel on the same stream.
+ * their log-sum-exps in a second kernel on the same stream (for more than 64 sequences a
+ * small planning kernel runs first). Nothing is allocated and nothing synchronises.
  * Requirements: page_size == 16 and d in {64, 128} (else FA_ERR_UNSUPPORTED);
  * H % Hkv == 0 and H / Hkv <= 16, or a multiple of 16; num_seqs, H, Hkv,
- * num_pages >= 1; max_pages_per_seq * page_size >= max_seq_len >= 1.
+ * num_pages >= 1; max_pages_per_seq * page_size >= max_seq_len >= 1;
+ * num_seqs <= 65535 and num_seqs * ceil(max_seq_len / 16) < 2^30 (else
+ * FA_ERR_UNSUPPORTED).
  * Device-side values: a seq_len outside [0, max_seq_len] is clamped into it; a
  * sequence with seq_len 0 gets O = 0 and lse = -inf; page ids outside
  * [0, num_pages) are never dereferenced (their tokens are skipped, so the result is
