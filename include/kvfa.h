@@ -148,8 +148,8 @@ int fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float*
  * Requirements: page_size == 16 and d in {64, 128} (else FA_ERR_UNSUPPORTED);
  * H % Hkv == 0 and H / Hkv <= 16, or a multiple of 16; num_seqs, H, Hkv,
  * num_pages >= 1; max_pages_per_seq * page_size >= max_seq_len >= 1;
- * num_seqs <= 65535 and num_seqs * ceil(max_seq_len / 16) < 2^30 (else
- * FA_ERR_UNSUPPORTED).
+ * num_seqs <= 65535 and num_seqs * ceil(max_seq_len / 16) <= 248 * 65535 (the pages the
+ * table can describe must fit the launch; else FA_ERR_UNSUPPORTED).
  * Device-side values: a seq_len outside [0, max_seq_len] is clamped into it; a
  * sequence with seq_len 0 gets O = 0 and lse = -inf; page ids outside
  * [0, num_pages) are never dereferenced (their tokens are skipped, so the result is
