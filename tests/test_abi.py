@@ -108,6 +108,9 @@ def _dec(lib, q=P, kc=P, vc=P, pt=P, sl=P, page_size=16, o=P, lse=None, S=4, H=3
     (dict(ws_bytes=16), INVALID),
     (dict(page_size=32, max_pages=4), UNSUPPORTED), (dict(d=80), UNSUPPORTED),
     (dict(H=40, Hkv=2), UNSUPPORTED),   # group of 20 query heads
+    (dict(S=65536), UNSUPPORTED),        # one combine row per sequence
+    # 8 sequences x 2031586 pages: one page more than 248 x 65535 work-group rows cover
+    (dict(S=8, max_seq_len=16 * 2031586, max_pages=2031586), UNSUPPORTED),
 ])
 def test_decode_validation(lib, kw, want):
     assert _dec(lib, **kw) == want
