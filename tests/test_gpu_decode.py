@@ -84,6 +84,7 @@ def test_decode_edge_lengths():
     (130, 8, 2, 64, 300, 512, 41),        # sequences read in three chunks of 64
     (200, 4, 1, 128, 40, 131072, 42),     # 248-page ranges, each spanning many sequences
     (97, 16, 4, 128, 2000, 4096, 43),     # a chunk boundary inside a range
+    (1500, 4, 1, 64, 40, 64, 45),         # the planning kernel's 1024-length passes, twice
 ], ids=lambda x: str(x))
 def test_decode_many_sequences(S, H, Hkv, d, hi, max_seq_len, seed):
     """More than 64 sequences (the in-kernel page count and prefix sums run over chunks of
