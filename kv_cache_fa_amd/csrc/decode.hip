@@ -70,7 +70,11 @@ DecodePlan decode_plan(int num_seqs, int max_seq_len) {
 // MFMA and V bytes to fp32 for the P.V FMAs; the K scale is folded into the softmax
 // scale and the V scale is applied to each partial result, so the arithmetic is that of
 // the dequantised cache. Each cached token costs half the bytes of the bf16 cache.
-template <int D, int GH, bool FP8>
+// PAIR (e4m3 cache, d = 128): a work-group serves two neighbouring KV heads, GH / 2 query
+// columns each, and reads their rows as one 256-byte row (two 128-byte rows of one token
+// are adjacent in the page): HBM serves 256-byte pieces faster than 128-byte ones. Q is
+// zero outside its own head's half of the row, so one score product covers both heads.
+template <int D, int GH, bool FP8, bool PAIR = false>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kcache,
     const void* __restrict__ vcache, const int32_t* __restrict__ page_table,
@@ -81,11 +85,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     int wg_target, float scale_log2_in, const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
     constexpr int ES = FP8 ? 1 : 2;    // bytes per cached element
     using KVec = std::conditional_t<FP8, u32x2, u32x4>;  // 8 cached elements
-    constexpr int CH = D / 8;          // 16-byte chunks per token row
+    constexpr int NK = PAIR ? 2 : 1;   // KV heads per work-group
+    constexpr int DR = NK * D;         // elements of one row read (token, NK KV heads)
+    constexpr int G2 = GH / NK;        // query columns per KV head
+    static_assert(!PAIR || (FP8 && GH == 8), "pairs: e4m3 cache, four columns per KV head");
+    constexpr int CH = DR / 8;         // 8-element chunks per row read
     constexpr int TG = 64 / CH;        // token groups of the P.V lane layout
     constexpr int TPL = kPage / TG;    // tokens per lane in P.V
-    constexpr int KS = D / 32;         // MFMA k-steps over the head dimension
-    constexpr int ROWB = D * ES;       // bytes of one cached row (token, KV head)
+    constexpr int KS = DR / 32;        // MFMA k-steps over the row
+    constexpr int ROWB = DR * ES;      // bytes of one row read
     constexpr int KCH = ROWB / 16;     // 16-byte chunks per row
     constexpr int PAGEB = kPage * ROWB;            // bytes of one page's K rows
     constexpr int KDMA = PAGEB / 1024;             // 1 KiB direct loads per page
@@ -106,7 +114,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     __shared__ float red_m[kWaves][GH];
     __shared__ float red_l[kWaves][GH];
 
-    const int kvh = blockIdx.x / n_hg, hg = blockIdx.x % n_hg;
+    const int kvh = NK * (blockIdx.x / n_hg), hg = blockIdx.x % n_hg;  // (first) KV head
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
     const int n = lane & 15;     // head column of S^T held by this lane
@@ -114,12 +122,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const int tg = lane / CH, c = lane % CH;  // P.V layout: token group, V chunk
     const int h0 = kvh * g + hg * GH;
     const int nheads = min(GH, g - hg * GH);
+    // Column n's KV head (of the NK) and query head, and whether that head exists.
+    const int kn = PAIR ? n / G2 : 0, hn = PAIR ? n % G2 : n;
+    const int head_n = PAIR ? (kvh + kn) * g + hn : h0 + n;
+    const bool col_ok = PAIR ? hn < g : n < nheads;
     const size_t tok_stride = (size_t)Hkv * D;  // elements between consecutive slots
     // Softmax scale in log2 units (times the K scale for an fp8 cache) and the V scale.
     float scale_log2 = scale_log2_in, v_sc = 1.f;
     if constexpr (FP8) {
-        scale_log2 *= k_scale[kvh];
-        v_sc = v_scale[kvh];
+        scale_log2 *= k_scale[kvh + kn];  // per column: the column's KV head
+        v_sc = v_scale[kvh];              // (pairs take theirs per column in the merge)
     }
     // Move the reference max past +8 in log2 units (with a zero K scale every score is 0:
     // the first page then moves the reference and every later one keeps it).
@@ -130,7 +142,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     // Loads are issued unconditionally (a zero-size descriptor for an invalid page id
     // makes them return zeros without touching memory), so the wait counts stay exact.
     // The cache is read once per call: the loads carry the nontemporal hint.
-    const uint32_t span = (uint32_t)((kPage - 1) * tok_stride + D) * ES;
+    const uint32_t span = (uint32_t)((kPage - 1) * tok_stride + DR) * ES;
     const uint32_t v_off = (uint32_t)(tg * tok_stride + c * 8) * ES;
     // K direct loads: lane L of the i-th 1 KiB piece fills stage byte 1024 i + 16 L, i.e.
     // row r, physical chunk pc, with logical chunk pc ^ (r % KCH) of cached row r.
@@ -164,15 +176,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
         qf[j] = u32x4{0, 0, 0, 0};
-        if (n < nheads)
-            qf[j] = *reinterpret_cast<const u32x4*>(q + ((size_t)s * H + h0 + n) * D +
-                                                     (j * 4 + kq) * 8);
+        const int kk = (j * 4 + kq) * 8;  // element of the row read
+        if (col_ok && kk / D == kn)       // a pair's column is zero in the other head's half
+            qf[j] = *reinterpret_cast<const u32x4*>(q + ((size_t)s * H + head_n) * D + kk - kn * D);
     }
 
     float m_used = -INFINITY, l_part = 0.f;
-    float oacc[GH][8];
+    // P.V: this lane's chunk c of the row belongs to KV head kc of the NK; it accumulates
+    // that head's G2 columns.
+    const int kc = PAIR ? c / (D / 8) : 0;
+    float oacc[G2][8];
 #pragma unroll
-    for (int hh = 0; hh < GH; ++hh)
+    for (int hh = 0; hh < G2; ++hh)
 #pragma unroll
         for (int e = 0; e < 8; ++e) oacc[hh][e] = 0.f;
 
@@ -255,8 +270,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 
             if (resc) {
 #pragma unroll
-                for (int hh = 0; hh < GH; ++hh) {
-                    const float a = a_lds[w][hh];
+                for (int hh = 0; hh < G2; ++hh) {
+                    const float a = a_lds[w][kc * G2 + hh];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) oacc[hh][e] *= a;
                 }
@@ -278,8 +293,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
                     }
                 }
 #pragma unroll
-                for (int hh = 0; hh < GH; ++hh) {
-                    const float p = p_lds[w][tl][hh];
+                for (int hh = 0; hh < G2; ++hh) {
+                    const float p = p_lds[w][tl][kc * G2 + hh];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) oacc[hh][e] = fmaf(p, x[e], oacc[hh][e]);
                 }
@@ -304,7 +319,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     l += shfl_xor(l, 16);
     l += shfl_xor(l, 32);
 #pragma unroll
-    for (int hh = 0; hh < GH; ++hh)
+    for (int hh = 0; hh < G2; ++hh)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float x = oacc[hh][e];
@@ -319,14 +334,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     if (tg == 0) {
         float* ro = red_o(w);
 #pragma unroll
-        for (int hh = 0; hh < GH; ++hh)
+        for (int hh = 0; hh < G2; ++hh)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ro[hh * D + c * 8 + e] = oacc[hh][e];
+            for (int e = 0; e < 8; ++e) ro[(kc * G2 + hh) * D + (c % (D / 8)) * 8 + e] = oacc[hh][e];
     }
     __syncthreads();
 
-    for (int idx = tid; idx < nheads * D; idx += 256) {
-        const int hh = idx / D, dd = idx % D;
+    for (int idx = tid; idx < (PAIR ? GH : nheads) * D; idx += 256) {
+        const int hh = idx / D, dd = idx % D;  // column, dim
+        if (PAIR && hh % G2 >= g) continue;    // a pair's padding column
+        // The column's scales (a pair's columns come from two KV heads).
+        const float sc = PAIR ? scale_log2_in * k_scale[kvh + hh / G2] : scale_log2;
+        const float vs = PAIR ? v_scale[kvh + hh / G2] : v_sc;
+        const int head = PAIR ? (kvh + hh / G2) * g + hh % G2 : h0 + hh;
         float M = -INFINITY;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red_m[ww][hh]);
@@ -335,15 +355,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
             for (int ww = 0; ww < kWaves; ++ww) {
                 const float mw = red_m[ww][hh];  // -inf for a wave that saw no token
-                const float f = mw == -INFINITY ? 0.f : fast_exp2((mw - M) * scale_log2);
+                const float f = mw == -INFINITY ? 0.f : fast_exp2((mw - M) * sc);
                 lsum = fmaf(f, red_l[ww][hh], lsum);
                 acc = fmaf(f, red_o(ww)[hh * D + dd], acc);
             }
         }
-        const size_t row = ((size_t)s * H + h0 + hh) * max_slots + slot;
-        o_part[row * D + dd] = M != -INFINITY ? acc / lsum * v_sc : 0.f;
+        const size_t row = ((size_t)s * H + head) * max_slots + slot;
+        o_part[row * D + dd] = M != -INFINITY ? acc / lsum * vs : 0.f;
         if (dd == 0)
-            lse_part[row] = M != -INFINITY ? M * scale_log2 + fast_log2(lsum) : -INFINITY;
+            lse_part[row] = M != -INFINITY ? M * sc + fast_log2(lsum) : -INFINITY;
     }
     __syncthreads();  // the next segment's loads overwrite the merge buffers
     };
@@ -586,13 +606,16 @@ int decode_target(int GH, bool fp8, int groups) {
     const int per_cu = GH == 4 ? 3 : GH == 8 ? 2 : 1;
     return std::max(1, per_cu * kCUs * (fp8 ? 2 : 1) / groups);
 }
+// Pairs (e4m3, d = 128): one round of 2 work-groups per CU (the pair kernel's register
+// use) over the KV head pairs; two or four rounds were slower.
+int decode_target_pair(int pairs) { return std::max(1, 2 * kCUs / pairs); }
 // The most work-groups per (KV head, head group) a launch can have, for any head count or
 // cache type: sizes the plan in the workspace.
 int decode_max_rows(const DecodePlan& plan, int num_seqs) {
     return std::max(std::max(3 * kCUs * 2, plan.min_wgs), num_seqs);
 }
 
-template <int D, int GH, bool FP8>
+template <int D, int GH, bool FP8, bool PAIR = false>
 hipError_t launch_split(const void* q, const void* kc, const void* vc, const int32_t* pt,
                         const int32_t* sl, const DecodeWorkspace& ws, const DecodePlan& plan,
                         int target, int rows, int num_seqs, int H, int Hkv, int g, int n_hg,
@@ -602,8 +625,8 @@ hipError_t launch_split(const void* q, const void* kc, const void* vc, const int
     // KV heads vary fastest: the work-groups covering one page range are dispatched
     // together, so each physical page (all KV heads of 16 slots, contiguous) is read by
     // concurrently running work-groups.
-    dim3 grid(Hkv * n_hg, rows);
-    hipLaunchKernelGGL((decode_split_kernel<D, GH, FP8>), grid, dim3(256), 0, stream,
+    dim3 grid(Hkv * n_hg / (PAIR ? 2 : 1), rows);
+    hipLaunchKernelGGL((decode_split_kernel<D, GH, FP8, PAIR>), grid, dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), kc, vc, pt, sl, ws.o_part, ws.lse_part,
                        ws.n_slots, num_seqs > 64 ? ws.plan : nullptr, num_seqs, H, Hkv, g, n_hg,
                        num_pages, max_pages, max_seq_len,
@@ -612,12 +635,17 @@ hipError_t launch_split(const void* q, const void* kc, const void* vc, const int
 }
 
 template <int D, bool FP8>
-hipError_t launch_split_d(int GH, const void* q, const void* kc, const void* vc,
+hipError_t launch_split_d(int GH, bool pair, const void* q, const void* kc, const void* vc,
                           const int32_t* pt, const int32_t* sl, const DecodeWorkspace& ws,
                           const DecodePlan& plan, int target, int rows, int num_seqs, int H,
                           int Hkv, int g, int n_hg, int num_pages, int max_pages,
                           int max_seq_len, float scale, const float* ks, const float* vs,
                           hipStream_t stream) {
+    if constexpr (FP8 && D == 128)
+        if (pair)
+            return launch_split<D, 8, true, true>(q, kc, vc, pt, sl, ws, plan, target, rows,
+                                                  num_seqs, H, Hkv, g, n_hg, num_pages,
+                                                  max_pages, max_seq_len, scale, ks, vs, stream);
     if (GH == 4)
         return launch_split<D, 4, FP8>(q, kc, vc, pt, sl, ws, plan, target, rows, num_seqs, H, Hkv, g, n_hg,
                                        num_pages, max_pages, max_seq_len, scale, ks, vs, stream);
@@ -664,7 +692,10 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
     const DecodePlan plan = decode_plan(num_seqs, max_seq_len);
     const DecodeWorkspace ws = decode_workspace(workspace, num_seqs, H, d, plan.max_slots);
 
-    const int target = decode_target(GH, fp8, Hkv * n_hg);
+    // An e4m3 cache with d = 128, an even KV head count and at most 4 query heads per KV
+    // head reads KV heads in pairs (256-byte rows).
+    const bool pair = fp8 && d == 128 && Hkv % 2 == 0 && g <= 4;
+    const int target = pair ? decode_target_pair(Hkv / 2) : decode_target(GH, fp8, Hkv * n_hg);
     const int rows = std::max(std::max(target, plan.min_wgs), num_seqs);  // <= decode_max_rows
 
     hipError_t e;
@@ -675,20 +706,20 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
         if (e != hipSuccess) return e;
     }
     if (d == 128)
-        e = fp8 ? launch_split_d<128, true>(GH, q, k_cache, v_cache, page_table, seq_lens, ws,
+        e = fp8 ? launch_split_d<128, true>(GH, pair, q, k_cache, v_cache, page_table, seq_lens, ws,
                                             plan, target, rows, num_seqs, H, Hkv, g, n_hg, num_pages,
                                             max_pages_per_seq, max_seq_len, scale, k_scale,
                                             v_scale, stream)
-                : launch_split_d<128, false>(GH, q, k_cache, v_cache, page_table, seq_lens, ws,
+                : launch_split_d<128, false>(GH, pair, q, k_cache, v_cache, page_table, seq_lens, ws,
                                              plan, target, rows, num_seqs, H, Hkv, g, n_hg, num_pages,
                                              max_pages_per_seq, max_seq_len, scale, nullptr,
                                              nullptr, stream);
     else
-        e = fp8 ? launch_split_d<64, true>(GH, q, k_cache, v_cache, page_table, seq_lens, ws,
+        e = fp8 ? launch_split_d<64, true>(GH, pair, q, k_cache, v_cache, page_table, seq_lens, ws,
                                            plan, target, rows, num_seqs, H, Hkv, g, n_hg, num_pages,
                                            max_pages_per_seq, max_seq_len, scale, k_scale,
                                            v_scale, stream)
-                : launch_split_d<64, false>(GH, q, k_cache, v_cache, page_table, seq_lens, ws,
+                : launch_split_d<64, false>(GH, pair, q, k_cache, v_cache, page_table, seq_lens, ws,
                                             plan, target, rows, num_seqs, H, Hkv, g, n_hg, num_pages,
                                             max_pages_per_seq, max_seq_len, scale, nullptr,
                                             nullptr, stream);
