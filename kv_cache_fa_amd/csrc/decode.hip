@@ -70,11 +70,11 @@ DecodePlan decode_plan(int num_seqs, int max_seq_len) {
 // MFMA and V bytes to fp32 for the P.V FMAs; the K scale is folded into the softmax
 // scale and the V scale is applied to each partial result, so the arithmetic is that of
 // the dequantised cache. Each cached token costs half the bytes of the bf16 cache.
-// PAIR (128-byte rows: an e4m3 cache with d = 128 or a bf16 one with d = 64): a work-group
-// serves two neighbouring KV heads, GH / 2 query columns each, and reads their rows as one
-// 256-byte row (two rows of one token are adjacent in the page): HBM serves 256-byte pieces
-// faster than 128-byte ones. Q is zero outside its own head's half of the row, so one score
-// product covers both heads.
+// PAIR: a work-group serves two neighbouring KV heads, GH / 2 query columns each, and reads
+// their rows as one row of twice the length (two rows of one token are adjacent in the
+// page): HBM serves longer contiguous pieces faster (128 -> 256 bytes for e4m3 with d = 128
+// or bf16 with d = 64, 256 -> 512 bytes for bf16 with d = 128). Q is zero outside its own
+// head's half of the row, so one score product covers both heads.
 template <int D, int GH, bool FP8, bool PAIR = false>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kcache,
@@ -89,7 +89,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     constexpr int NK = PAIR ? 2 : 1;   // KV heads per work-group
     constexpr int DR = NK * D;         // elements of one row read (token, NK KV heads)
     constexpr int G2 = GH / NK;        // query columns per KV head
-    static_assert(!PAIR || (GH == 8 && D * ES == 128), "pairs: 128-byte rows, four columns per KV head");
+    static_assert(!PAIR || (GH == 8 && (D * ES == 128 || D * ES == 256)),
+                  "pairs: 128- or 256-byte rows, four query columns per KV head");
     constexpr int CH = DR / 8;         // 8-element chunks per row read
     constexpr int TG = 64 / CH;        // token groups of the P.V lane layout
     constexpr int TPL = kPage / TG;    // tokens per lane in P.V
@@ -608,10 +609,12 @@ int decode_target(int GH, bool fp8, int groups) {
     const int per_cu = GH == 4 ? 3 : GH == 8 ? 2 : 1;
     return std::max(1, per_cu * kCUs * (fp8 ? 2 : 1) / groups);
 }
-// Pairs: one round of the pair kernel's work-groups per CU (2 for e4m3 with d = 128, 3 for
-// bf16 with d = 64, by their register use) over the KV head pairs; two or four rounds
-// were slower.
-int decode_target_pair(int pairs, bool fp8) { return std::max(1, (fp8 ? 2 : 3) * kCUs / pairs); }
+// Pairs: one round of the pair kernel's work-groups per CU (3 for bf16 with d = 64, else 2,
+// by their register use) over the KV head pairs; two or four rounds were slower.
+int decode_target_pair(int pairs, bool fp8, int d) {
+    const int per_cu = !fp8 && d == 64 ? 3 : 2;
+    return std::max(1, per_cu * kCUs / pairs);
+}
 // The most work-groups per (KV head, head group) a launch can have, for any head count or
 // cache type: sizes the plan in the workspace.
 int decode_max_rows(const DecodePlan& plan, int num_seqs) {
@@ -644,7 +647,7 @@ hipError_t launch_split_d(int GH, bool pair, const void* q, const void* kc, cons
                           int Hkv, int g, int n_hg, int num_pages, int max_pages,
                           int max_seq_len, float scale, const float* ks, const float* vs,
                           hipStream_t stream) {
-    if constexpr (D * (FP8 ? 1 : 2) == 128)
+    if constexpr (D * (FP8 ? 1 : 2) == 128 || (!FP8 && D == 128))
         if (pair)
             return launch_split<D, 8, FP8, true>(q, kc, vc, pt, sl, ws, plan, target, rows,
                                                   num_seqs, H, Hkv, g, n_hg, num_pages,
@@ -695,10 +698,14 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
     const DecodePlan plan = decode_plan(num_seqs, max_seq_len);
     const DecodeWorkspace ws = decode_workspace(workspace, num_seqs, H, d, plan.max_slots);
 
-    // 128-byte rows (an e4m3 cache with d = 128, a bf16 one with d = 64), an even KV head
-    // count and at most 4 query heads per KV head: KV heads are read in pairs (256-byte rows).
-    const bool pair = d * (fp8 ? 1 : 2) == 128 && Hkv % 2 == 0 && g <= 4;
-    const int target = pair ? decode_target_pair(Hkv / 2, fp8) : decode_target(GH, fp8, Hkv * n_hg);
+    // An even KV head count and at most 4 query heads per KV head: KV heads are read in
+    // pairs (128-byte rows of an e4m3 cache with d = 128 or a bf16 one with d = 64 become
+    // 256-byte rows; bf16 rows with d = 128 become 512-byte rows).
+    // Small batches (under 32 sequences) keep single heads: their work-groups are few, and
+    // pairs would halve them (1 x 8192 tokens, H32 Hkv8 d128: 15.3 us single, 16.6 paired).
+    const bool pair = (d * (fp8 ? 1 : 2) == 128 || (!fp8 && d == 128)) && Hkv % 2 == 0 &&
+                      g <= 4 && num_seqs >= 32;
+    const int target = pair ? decode_target_pair(Hkv / 2, fp8, d) : decode_target(GH, fp8, Hkv * n_hg);
     const int rows = std::max(std::max(target, plan.min_wgs), num_seqs);  // <= decode_max_rows
 
     hipError_t e;

@@ -99,10 +99,11 @@ def test_decode_many_sequences(S, H, Hkv, d, hi, max_seq_len, seed):
         assert np.all(inputs.bf16_bits_to_f32(o_h[s]) == 0.0) and np.all(lse_h[s] == -np.inf)
 
 
-def test_unused_slots_and_table_padding_are_never_read():
+@pytest.mark.parametrize("S", [12, 40])  # 40: KV heads read in pairs
+def test_unused_slots_and_table_padding_are_never_read(S):
     """Slots past a sequence's length hold NaN and unused table entries hold -1: the
     output must be bit-identical to the zero-filled cache's."""
-    cfg = inputs.DecodeConfig("nan", 12, 16, 4, 128, 1, 900, 16, 1024, 1 / math.sqrt(128), 11)
+    cfg = inputs.DecodeConfig("nan", S, 16, 4, 128, 1, 900, 16, 1024, 1 / math.sqrt(128), 11)
     a = inputs.make_decode(cfg)
     b = inputs.make_decode(cfg, unused_fill="nan", table_pad=-1)
     assert np.array_equal(a.seq_lens, b.seq_lens)
@@ -114,11 +115,12 @@ def test_unused_slots_and_table_padding_are_never_read():
     check_bf16(inputs.bf16_bits_to_f64(ob), lb, O, L, "nan-filled cache")
 
 
-def test_peaked_query_selects_cached_value_bit_exactly():
+@pytest.mark.parametrize("S", [16, 40])  # 40: KV heads read in pairs
+def test_peaked_query_selects_cached_value_bit_exactly(S):
     """q[s,h] = 64 * K_s[t*] for a seeded target token t* per (sequence, head): every
     other exponential underflows to exactly 0, so O[s,h] must equal the stored
     V_s[t*] bit for bit. A wrong page, slot or head index cannot pass."""
-    cfg = inputs.DecodeConfig("peak", 16, 32, 8, 128, 1, 3000, 16, 3000, 1 / math.sqrt(128), 17)
+    cfg = inputs.DecodeConfig("peak", S, 32, 8, 128, 1, 3000, 16, 3000, 1 / math.sqrt(128), 17)
     inp = inputs.make_decode(cfg)
     rng = np.random.default_rng(99)
     g = cfg.H // cfg.Hkv
