@@ -85,6 +85,8 @@ def test_decode_edge_lengths():
     (200, 4, 1, 128, 40, 131072, 42),     # 248-page ranges, each spanning many sequences
     (97, 16, 4, 128, 2000, 4096, 43),     # a chunk boundary inside a range
     (1500, 4, 1, 64, 40, 64, 45),         # the planning kernel's 1024-length passes, twice
+    (48, 8, 8, 128, 600, 1024, 46),       # KV head pairs with g = 1 (3 padding columns each)
+    (40, 16, 8, 64, 500, 1024, 47),       # pairs, g = 2, d = 64
 ], ids=lambda x: str(x))
 def test_decode_many_sequences(S, H, Hkv, d, hi, max_seq_len, seed):
     """More than 64 sequences (the in-kernel page count and prefix sums run over chunks of

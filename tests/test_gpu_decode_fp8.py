@@ -98,6 +98,12 @@ def test_fp8_decode_many_sequences():
         assert np.all(inputs.bf16_bits_to_f32(o_h[s]) == 0.0) and np.all(lse_h[s] == -np.inf)
 
 
+def test_fp8_decode_pairs_with_padding_columns():
+    """40 sequences, H8 Hkv4 (g = 2): KV heads read in pairs, two padding columns per head."""
+    base = inputs.custom_decode(40, 8, 4, 128, 1, 900, seed=48)
+    _check(inputs.quantize_decode_fp8(base), "fp8 pairs g=2")
+
+
 def test_fp8_edge_lengths_and_nan_slots():
     """Empty sequence, page boundaries; unused slots hold e4m3 NaN bytes and the table is
     padded with -1: the output must equal the zero-filled cache's bit for bit."""
