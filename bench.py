@@ -156,8 +156,8 @@ def main(argv=None):
     dsl = torch.from_numpy(dinp.seq_lens).to(dev)
     do = torch.empty_like(dq)
     dlse = torch.empty((dcfg.num_seqs, dcfg.H), dtype=torch.float32, device=dev)
-    ws = torch.empty(_lib.fa_decode_paged_workspace_size(dcfg.num_seqs, dcfg.H, dcfg.Hkv,
-                                                         dcfg.d, dcfg.max_seq_len), dtype=torch.uint8,
+    ws = torch.empty(_lib.fa_decode_paged_workspace_size(dcfg.num_seqs, dcfg.H, dcfg.d,
+                                                         dcfg.max_seq_len), dtype=torch.uint8,
                      device=dev)
     torch.cuda.synchronize()
 

@@ -18,7 +18,8 @@
  * - Every tensor is dense and row-major with the head dimension d innermost; there
  *   are no stride arguments. bf16 tensors are passed as raw 16-bit patterns.
  * - Tensor pointers must be 16-byte aligned. lse may be NULL (then it is not written).
- * - stream is a hipStream_t (NULL = the default stream). Work is only enqueued: a
+ * - stream is the HIP stream the work is enqueued on (NULL = the default stream) and
+ *   must belong to the current device, as for any HIP call. Work is only enqueued: a
  *   return of FA_OK means "launched", device-side results are ready after the
  *   caller synchronises the stream.
  * - Errors: invalid arguments return FA_ERR_INVALID or FA_ERR_UNSUPPORTED before
@@ -36,6 +37,8 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
 
 #ifdef __cplusplus
 extern "C" {
@@ -61,7 +64,7 @@ typedef enum {
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-           void* stream);
+           hipStream_t stream);
 
 /*
  * fa_bwd — gradients of fa_fwd's output with respect to q, k and v, recomputing the
@@ -85,7 +88,7 @@ size_t fa_bwd_workspace_size(int B, int H, int Nq);
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq,
            int Nk, int d, int causal, float scale, void* workspace, size_t workspace_bytes,
-           void* stream);
+           hipStream_t stream);
 
 /*
  * fa_fwd_two_pass — fa_fwd computed in the two passes of FlashAttention-1 (page
@@ -102,7 +105,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
  */
 int fa_fwd_two_pass(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-                    void* stream);
+                    hipStream_t stream);
 
 /*
  * fa_fwd_window — fa_fwd with a sliding-window mask (glossary entry "Kayan Pencere
@@ -118,7 +121,7 @@ int fa_fwd_two_pass(const void* q, const void* k, const void* v, void* o, float*
  */
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int Hkv, int Nq, int Nk, int d, int window_left,
-                  int window_right, float scale, void* stream);
+                  int window_right, float scale, hipStream_t stream);
 
 /*
  * fa_fwd_fp32 — the same operation with fp32 inputs and outputs and fp32 arithmetic
@@ -126,7 +129,7 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
  */
 int fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse,
                 int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-                void* stream);
+                hipStream_t stream);
 
 /*
  * fa_decode_paged — one new query token per sequence against a paged KV cache
@@ -156,14 +159,14 @@ int fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float*
  * then not meaningful). Table entries past a sequence's last page and page slots
  * past its length are never read.
  */
-size_t fa_decode_paged_workspace_size(int num_seqs, int H, int Hkv, int d,
-                                      int max_seq_len, int page_size);
+size_t fa_decode_paged_workspace_size(int num_seqs, int H, int d, int max_seq_len,
+                                      int page_size);
 
 int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* page_table, const int32_t* seq_lens, int page_size,
                     void* o, float* lse, int num_seqs, int H, int Hkv, int d,
                     int num_pages, int max_pages_per_seq, int max_seq_len, float scale,
-                    void* workspace, size_t workspace_bytes, void* stream);
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * fa_decode_paged_fp8 — fa_decode_paged on a cache stored in 8-bit floating point
@@ -184,7 +187,7 @@ int fa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* page_table, const int32_t* seq_lens, int page_size,
                         void* o, float* lse, int num_seqs, int H, int Hkv, int d,
                         int num_pages, int max_pages_per_seq, int max_seq_len, float scale,
-                        void* workspace, size_t workspace_bytes, void* stream);
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The fewest cached tokens one split-K work-group's range holds for these sizes (a
  * multiple of the page size: 4 pages, or 1/32 of max_seq_len's pages, at most 248 pages).
@@ -194,7 +197,7 @@ int fa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
  * per head, plus one int32 per sequence (its slot count) and a plan of 4 + 2 x max(1536,
  * ceil(num_seqs x max_pages / 248), num_seqs) int32 (for more than 64 sequences a small
  * planning kernel writes where each work-group's range starts). */
-int fa_decode_paged_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size);
+int fa_decode_paged_split_tokens(int num_seqs, int max_seq_len, int page_size);
 
 /*
  * fa_fwd_paged — chunked prefill: bf16 attention of Nq new queries per sequence against
@@ -220,7 +223,7 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
                  const int32_t* page_table, const int32_t* seq_lens, int page_size, void* o,
                  float* lse, int B, int H, int Hkv, int Nq, int d, int num_pages,
                  int max_pages_per_seq, int max_seq_len, int causal, float scale,
-                 void* stream);
+                 hipStream_t stream);
 
 /*
  * fa_kv_append — store the keys and values of n_new new tokens per sequence in the
@@ -245,7 +248,7 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
 int fa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                  const int32_t* page_table, const int32_t* start_pos, int page_size,
                  int num_seqs, int n_new, int Hkv, int d, int num_pages,
-                 int max_pages_per_seq, void* stream);
+                 int max_pages_per_seq, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* fa_status_string(int status);

@@ -22,8 +22,8 @@ _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_
 SIGNATURES = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp]),
     "fa_fwd_fp32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp]),
-    "fa_decode_paged_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
-    "fa_decode_paged_split_tokens": (_i, [_i, _i, _i, _i]),
+    "fa_decode_paged_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "fa_decode_paged_split_tokens": (_i, [_i, _i, _i]),
     "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                              _f, _vp, _sz, _vp]),
     "fa_fwd_two_pass": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp]),
@@ -173,12 +173,12 @@ def fa_fwd_fp32(q, k, v, o, lse=None, *, causal: bool, scale: float, stream=None
                                             _stream(stream)))
 
 
-def fa_decode_paged_workspace_size(num_seqs, H, Hkv, d, max_seq_len, page_size=16) -> int:
-    return int(lib().fa_decode_paged_workspace_size(num_seqs, H, Hkv, d, max_seq_len, page_size))
+def fa_decode_paged_workspace_size(num_seqs, H, d, max_seq_len, page_size=16) -> int:
+    return int(lib().fa_decode_paged_workspace_size(num_seqs, H, d, max_seq_len, page_size))
 
 
-def fa_decode_paged_split_tokens(num_seqs, Hkv, max_seq_len, page_size=16) -> int:
-    return int(lib().fa_decode_paged_split_tokens(num_seqs, Hkv, max_seq_len, page_size))
+def fa_decode_paged_split_tokens(num_seqs, max_seq_len, page_size=16) -> int:
+    return int(lib().fa_decode_paged_split_tokens(num_seqs, max_seq_len, page_size))
 
 
 def fa_decode_paged(q, k_cache, v_cache, page_table, seq_lens, o, lse=None, *, max_seq_len: int,

@@ -6,7 +6,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
-#include "../../include/kvfa.h"
+#include "kvfa.h"
 #include "launch.h"
 
 namespace {
@@ -47,7 +47,7 @@ int decode_checked(const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* page_table, const int32_t* seq_lens, int page_size, void* o,
                    float* lse, int num_seqs, int H, int Hkv, int d, int num_pages,
                    int max_pages_per_seq, int max_seq_len, float scale, void* workspace,
-                   size_t workspace_bytes, void* stream, const float* k_scale,
+                   size_t workspace_bytes, hipStream_t stream, const float* k_scale,
                    const float* v_scale);
 
 }  // namespace
@@ -55,19 +55,19 @@ int decode_checked(const void* q, const void* k_cache, const void* v_cache,
 extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-           int Hkv, int Nq, int Nk, int d, int causal, float scale, void* stream) {
+           int Hkv, int Nq, int Nk, int d, int causal, float scale, hipStream_t stream) {
     int st = check_prefill(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale, 2);
     if (st != FA_OK) return st;
     const unsigned long long n_wg = (unsigned long long)((Nq + 127) / 128) * B * H;
     if (n_wg >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
     hipError_t e = kvfa::launch_fwd_bf16(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal != 0, scale,
-                                         static_cast<hipStream_t>(stream));
+                                         stream);
     return hip_status(e, "fa_fwd");
 }
 
 int fa_fwd_two_pass(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                     int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-                    void* stream) {
+                    hipStream_t stream) {
     if (!lse) return FA_ERR_INVALID;  // carries the row statistics between the passes
     int st = check_prefill(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale, 2);
     if (st != FA_OK) return st;
@@ -75,13 +75,13 @@ int fa_fwd_two_pass(const void* q, const void* k, const void* v, void* o, float*
     if (n_wg >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
     hipError_t e = kvfa::launch_fwd_bf16_two_pass(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d,
                                                   causal != 0, scale,
-                                                  static_cast<hipStream_t>(stream));
+                                                  stream);
     return hip_status(e, "fa_fwd_two_pass");
 }
 
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                   int H, int Hkv, int Nq, int Nk, int d, int window_left, int window_right,
-                  float scale, void* stream) {
+                  float scale, hipStream_t stream) {
     // The window is placed at each query's position Nk - Nq + i, so Nq <= Nk as for causal.
     int st = check_prefill(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, 1, scale, 2);
     if (st != FA_OK) return st;
@@ -90,37 +90,37 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
     if (n_wg >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
     hipError_t e = kvfa::launch_fwd_bf16_window(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d,
                                                 window_left, window_right, scale,
-                                                static_cast<hipStream_t>(stream));
+                                                stream);
     return hip_status(e, "fa_fwd_window");
 }
 
 int fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
-                int H, int Hkv, int Nq, int Nk, int d, int causal, float scale, void* stream) {
+                int H, int Hkv, int Nq, int Nk, int d, int causal, float scale, hipStream_t stream) {
     int st = check_prefill(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale, 4);
     if (st != FA_OK) return st;
     if (H > 65535 || B > 65535) return FA_ERR_UNSUPPORTED;
     hipError_t e = kvfa::launch_fwd_fp32(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal != 0, scale,
-                                         static_cast<hipStream_t>(stream));
+                                         stream);
     return hip_status(e, "fa_fwd_fp32");
 }
 
-int fa_decode_paged_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size) {
-    if (num_seqs < 1 || Hkv < 1 || max_seq_len < 1 || page_size != 16) return 0;
-    return kvfa::decode_split_tokens(num_seqs, Hkv, max_seq_len, page_size);
+int fa_decode_paged_split_tokens(int num_seqs, int max_seq_len, int page_size) {
+    if (num_seqs < 1 || max_seq_len < 1 || page_size != 16) return 0;
+    return kvfa::decode_split_tokens(num_seqs, max_seq_len);
 }
 
-size_t fa_decode_paged_workspace_size(int num_seqs, int H, int Hkv, int d, int max_seq_len,
+size_t fa_decode_paged_workspace_size(int num_seqs, int H, int d, int max_seq_len,
                                       int page_size) {
-    if (num_seqs < 1 || H < 1 || Hkv < 1 || max_seq_len < 1 || page_size != 16) return 0;
+    if (num_seqs < 1 || H < 1 || max_seq_len < 1 || page_size != 16) return 0;
     if (d != 64 && d != 128) return 0;
-    return kvfa::decode_workspace_bytes(num_seqs, H, Hkv, d, max_seq_len, page_size);
+    return kvfa::decode_workspace_bytes(num_seqs, H, d, max_seq_len);
 }
 
 int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* page_table, const int32_t* seq_lens, int page_size, void* o,
                     float* lse, int num_seqs, int H, int Hkv, int d, int num_pages,
                     int max_pages_per_seq, int max_seq_len, float scale, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    size_t workspace_bytes, hipStream_t stream) {
     return decode_checked(q, k_cache, v_cache, page_table, seq_lens, page_size, o, lse, num_seqs,
                           H, Hkv, d, num_pages, max_pages_per_seq, max_seq_len, scale, workspace,
                           workspace_bytes, stream, nullptr, nullptr);
@@ -133,7 +133,7 @@ int decode_checked(const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* page_table, const int32_t* seq_lens, int page_size, void* o,
                    float* lse, int num_seqs, int H, int Hkv, int d, int num_pages,
                    int max_pages_per_seq, int max_seq_len, float scale, void* workspace,
-                   size_t workspace_bytes, void* stream, const float* k_scale,
+                   size_t workspace_bytes, hipStream_t stream, const float* k_scale,
                    const float* v_scale) {
     if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !o || !workspace)
         return FA_ERR_INVALID;
@@ -156,12 +156,15 @@ int decode_checked(const void* q, const void* k_cache, const void* v_cache,
     if ((long long)num_seqs * ((max_seq_len + page_size - 1) / page_size) >= (1LL << 30) ||
         kvfa::decode_min_work_groups(num_seqs, max_seq_len) > 65535)
         return FA_ERR_UNSUPPORTED;
-    if (workspace_bytes < kvfa::decode_workspace_bytes(num_seqs, H, Hkv, d, max_seq_len, page_size))
+    if (workspace_bytes < kvfa::decode_workspace_bytes(num_seqs, H, d, max_seq_len))
         return FA_ERR_INVALID;
+    // The cache type travels with the scales: an e4m3 cache has both, a bf16 one neither.
+    if ((k_scale == nullptr) != (v_scale == nullptr)) return FA_ERR_INVALID;
+    const kvfa::DecodeCache cache = k_scale ? kvfa::DecodeCache::kFp8 : kvfa::DecodeCache::kBf16;
     hipError_t e = kvfa::launch_decode_paged(q, k_cache, v_cache, page_table, seq_lens, o, lse,
                                              num_seqs, H, Hkv, d, num_pages, max_pages_per_seq,
-                                             max_seq_len, scale, workspace,
-                                             static_cast<hipStream_t>(stream), k_scale, v_scale);
+                                             max_seq_len, scale, workspace, stream, cache,
+                                             k_scale, v_scale);
     return hip_status(e, "decode_checked");
 }
 }  // namespace
@@ -172,7 +175,7 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
                  const int32_t* page_table, const int32_t* seq_lens, int page_size, void* o,
                  float* lse, int B, int H, int Hkv, int Nq, int d, int num_pages,
                  int max_pages_per_seq, int max_seq_len, int causal, float scale,
-                 void* stream) {
+                 hipStream_t stream) {
     if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !o) return FA_ERR_INVALID;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
         !aligned(page_table, 4) || !aligned(seq_lens, 4))
@@ -191,14 +194,14 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
     hipError_t e = kvfa::launch_fwd_bf16_paged(q, k_cache, v_cache, page_table, seq_lens, o, lse,
                                                B, H, Hkv, Nq, d, num_pages, max_pages_per_seq,
                                                max_seq_len, causal != 0, scale,
-                                               static_cast<hipStream_t>(stream));
+                                               stream);
     return hip_status(e, "fa_fwd_paged");
 }
 
 int fa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                  const int32_t* page_table, const int32_t* start_pos, int page_size,
                  int num_seqs, int n_new, int Hkv, int d, int num_pages,
-                 int max_pages_per_seq, void* stream) {
+                 int max_pages_per_seq, hipStream_t stream) {
     if (!k_new || !v_new || !k_cache || !v_cache || !page_table || !start_pos)
         return FA_ERR_INVALID;
     if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
@@ -209,7 +212,7 @@ int fa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_ca
     if (page_size != 16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
     hipError_t e = kvfa::launch_kv_append(k_new, v_new, k_cache, v_cache, page_table, start_pos,
                                           num_seqs, n_new, Hkv, d, num_pages, max_pages_per_seq,
-                                          static_cast<hipStream_t>(stream));
+                                          stream);
     return hip_status(e, "fa_kv_append");
 }
 
@@ -221,7 +224,7 @@ size_t fa_bwd_workspace_size(int B, int H, int Nq) {
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq, int Nk,
            int d, int causal, float scale, void* workspace, size_t workspace_bytes,
-           void* stream) {
+           hipStream_t stream) {
     int st = check_prefill(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale, 2);
     if (st != FA_OK) return st;
     if (!lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_INVALID;
@@ -234,7 +237,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
     if (n_q >= (1ull << 31) || n_k >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
     hipError_t e = kvfa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, Nq, Nk, d,
                                          causal != 0, scale, workspace,
-                                         static_cast<hipStream_t>(stream));
+                                         stream);
     return hip_status(e, "fa_bwd");
 }
 
@@ -243,7 +246,7 @@ int fa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* page_table, const int32_t* seq_lens, int page_size,
                         void* o, float* lse, int num_seqs, int H, int Hkv, int d,
                         int num_pages, int max_pages_per_seq, int max_seq_len, float scale,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4))
         return FA_ERR_INVALID;
     return decode_checked(q, k_cache, v_cache, page_table, seq_lens, page_size, o, lse, num_seqs,

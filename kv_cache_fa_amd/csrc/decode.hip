@@ -75,6 +75,11 @@ DecodePlan decode_plan(int num_seqs, int max_seq_len) {
 // page): HBM serves longer contiguous pieces faster (128 -> 256 bytes for e4m3 with d = 128
 // or bf16 with d = 64, 256 -> 512 bytes for bf16 with d = 128). Q is zero outside its own
 // head's half of the row, so one score product covers both heads.
+// Per-KV-head scale arrays exist only for an e4m3 cache: the bf16 instantiations take
+// nullptr_t in their place, so no code path of theirs can read through one.
+template <bool FP8>
+using ScalePtr = std::conditional_t<FP8, const float*, std::nullptr_t>;
+
 template <int D, int GH, bool FP8, bool PAIR = false>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kcache,
@@ -83,7 +88,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     float* __restrict__ lse_part, int* __restrict__ n_slots, const int* __restrict__ plan,
     int num_seqs, int H, int Hkv,
     int g, int n_hg, int num_pages, int max_pages, int max_seq_len, int rmin, int max_slots,
-    int wg_target, float scale_log2_in, const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+    int wg_target, float scale_log2_in, ScalePtr<FP8> k_scale, ScalePtr<FP8> v_scale) {
     constexpr int ES = FP8 ? 1 : 2;    // bytes per cached element
     using KVec = std::conditional_t<FP8, u32x2, u32x4>;  // 8 cached elements
     constexpr int NK = PAIR ? 2 : 1;   // KV heads per work-group
@@ -124,10 +129,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const int tg = lane / CH, c = lane % CH;  // P.V layout: token group, V chunk
     const int h0 = kvh * g + hg * GH;
     const int nheads = min(GH, g - hg * GH);
-    // Column n's KV head (of the NK) and query head, and whether that head exists.
-    const int kn = PAIR ? n / G2 : 0, hn = PAIR ? n % G2 : n;
+    // Column n's KV head (of the NK) and query head, and whether that head exists. The
+    // MFMA has 16 columns; columns n >= GH are padding: they take the last KV head of the
+    // work-group (so every per-head array they index stays in range) and are never
+    // valid, so their Q stays zero and nothing of theirs is stored.
+    const int kn = PAIR ? min(n / G2, NK - 1) : 0, hn = PAIR ? n % G2 : n;
     const int head_n = PAIR ? (kvh + kn) * g + hn : h0 + n;
-    const bool col_ok = PAIR ? hn < g : n < nheads;
+    const bool col_ok = PAIR ? (n < GH && hn < g) : n < nheads;
     const size_t tok_stride = (size_t)Hkv * D;  // elements between consecutive slots
     // Softmax scale in log2 units (times the K scale for an fp8 cache) and the V scale.
     float scale_log2 = scale_log2_in, v_sc = 1.f;
@@ -347,8 +355,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         if (PAIR && hh % G2 >= g) continue;    // a pair's padding column
         // The column's scales (a pair's columns come from two KV heads).
         // (bf16 caches have no scale arrays: their columns share scale_log2 and v_sc = 1.)
-        const float sc = PAIR && FP8 ? scale_log2_in * k_scale[kvh + hh / G2] : scale_log2;
-        const float vs = PAIR && FP8 ? v_scale[kvh + hh / G2] : v_sc;
+        float sc = scale_log2, vs = v_sc;
+        if constexpr (PAIR && FP8) {
+            sc = scale_log2_in * k_scale[kvh + hh / G2];
+            vs = v_scale[kvh + hh / G2];
+        }
         const int head = PAIR ? (kvh + hh / G2) * g + hh % G2 : h0 + hh;
         float M = -INFINITY;
 #pragma unroll
@@ -626,7 +637,7 @@ hipError_t launch_split(const void* q, const void* kc, const void* vc, const int
                         const int32_t* sl, const DecodeWorkspace& ws, const DecodePlan& plan,
                         int target, int rows, int num_seqs, int H, int Hkv, int g, int n_hg,
                         int num_pages, int max_pages, int max_seq_len, float scale,
-                        const float* k_scale, const float* v_scale, hipStream_t stream) {
+                        ScalePtr<FP8> k_scale, ScalePtr<FP8> v_scale, hipStream_t stream) {
     const float scale_log2 = scale * kLog2e;
     // KV heads vary fastest: the work-groups covering one page range are dispatched
     // together, so each physical page (all KV heads of 16 slots, contiguous) is read by
@@ -645,7 +656,7 @@ hipError_t launch_split_d(int GH, bool pair, const void* q, const void* kc, cons
                           const int32_t* pt, const int32_t* sl, const DecodeWorkspace& ws,
                           const DecodePlan& plan, int target, int rows, int num_seqs, int H,
                           int Hkv, int g, int n_hg, int num_pages, int max_pages,
-                          int max_seq_len, float scale, const float* ks, const float* vs,
+                          int max_seq_len, float scale, ScalePtr<FP8> ks, ScalePtr<FP8> vs,
                           hipStream_t stream) {
     if constexpr (D * (FP8 ? 1 : 2) == 128 || (!FP8 && D == 128))
         if (pair)
@@ -664,9 +675,7 @@ hipError_t launch_split_d(int GH, bool pair, const void* q, const void* kc, cons
 
 }  // namespace
 
-int decode_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size) {
-    (void)page_size;
-    (void)Hkv;
+int decode_split_tokens(int num_seqs, int max_seq_len) {
     return decode_plan(num_seqs, max_seq_len).rmin * kPage;
 }
 
@@ -674,10 +683,7 @@ int decode_min_work_groups(int num_seqs, int max_seq_len) {
     return decode_plan(num_seqs, max_seq_len).min_wgs;
 }
 
-size_t decode_workspace_bytes(int num_seqs, int H, int Hkv, int d, int max_seq_len,
-                              int page_size) {
-    (void)page_size;
-    (void)Hkv;
+size_t decode_workspace_bytes(int num_seqs, int H, int d, int max_seq_len) {
     const DecodePlan plan = decode_plan(num_seqs, max_seq_len);
     const size_t rows = (size_t)num_seqs * H * plan.max_slots;
     return rows * (size_t)d * sizeof(float) + rows * sizeof(float) +
@@ -689,9 +695,10 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
                                const int32_t* page_table, const int32_t* seq_lens, void* o,
                                float* lse, int num_seqs, int H, int Hkv, int d, int num_pages,
                                int max_pages_per_seq, int max_seq_len, float scale,
-                               void* workspace, hipStream_t stream, const float* k_scale,
-                               const float* v_scale) {
-    const bool fp8 = k_scale != nullptr;
+                               void* workspace, hipStream_t stream, DecodeCache cache,
+                               const float* k_scale, const float* v_scale) {
+    const bool fp8 = cache == DecodeCache::kFp8;
+    if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return hipErrorInvalidValue;
     const int g = H / Hkv;
     const int GH = g <= 4 ? 4 : g <= 8 ? 8 : 16;
     const int n_hg = g <= 16 ? 1 : g / 16;

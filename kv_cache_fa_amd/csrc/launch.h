@@ -47,16 +47,21 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
 // Decode range plan: the fewest cached tokens a split-K work-group's range holds, the
 // work-groups per (KV head, head group) the longest possible cache needs, and the
 // workspace the plan implies.
-int decode_split_tokens(int num_seqs, int Hkv, int max_seq_len, int page_size);
+// (16-token pages throughout.)
+int decode_split_tokens(int num_seqs, int max_seq_len);
 int decode_min_work_groups(int num_seqs, int max_seq_len);
-size_t decode_workspace_bytes(int num_seqs, int H, int Hkv, int d, int max_seq_len,
-                              int page_size);
+size_t decode_workspace_bytes(int num_seqs, int H, int d, int max_seq_len);
+
+// Element type of the paged cache. An e4m3 cache comes with its per-KV-head scales
+// (k_scale, v_scale non-null); a bf16 cache has none (both null). The launcher returns
+// hipErrorInvalidValue, enqueueing nothing, when the pointers do not match the type.
+enum class DecodeCache { kBf16, kFp8 };
 
 hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* page_table, const int32_t* seq_lens, void* o,
                                float* lse, int num_seqs, int H, int Hkv, int d, int num_pages,
                                int max_pages_per_seq, int max_seq_len, float scale,
-                               void* workspace, hipStream_t stream,
-                               const float* k_scale = nullptr, const float* v_scale = nullptr);
+                               void* workspace, hipStream_t stream, DecodeCache cache,
+                               const float* k_scale, const float* v_scale);
 
 }  // namespace kvfa

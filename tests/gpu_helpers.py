@@ -66,7 +66,7 @@ class DecodeDev:
         self.sl = torch.from_numpy(inp.seq_lens).cuda()
         self.o = torch.empty_like(self.q)
         self.lse = torch.empty((c.num_seqs, c.H), dtype=torch.float32, device="cuda")
-        ws = _lib.fa_decode_paged_workspace_size(c.num_seqs, c.H, c.Hkv, c.d, c.max_seq_len,
+        ws = _lib.fa_decode_paged_workspace_size(c.num_seqs, c.H, c.d, c.max_seq_len,
                                                  c.page_size)
         self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
 

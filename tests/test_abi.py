@@ -92,7 +92,7 @@ def test_window_validation(lib, kw, want):
 def _dec(lib, q=P, kc=P, vc=P, pt=P, sl=P, page_size=16, o=P, lse=None, S=4, H=32, Hkv=8,
          d=128, num_pages=100, max_pages=8, max_seq_len=128, scale=0.09, ws=P, ws_bytes=None):
     if ws_bytes is None:
-        ws_bytes = lib.fa_decode_paged_workspace_size(S, H, Hkv, d, max_seq_len, page_size) \
+        ws_bytes = lib.fa_decode_paged_workspace_size(S, H, d, max_seq_len, page_size) \
             if page_size == 16 and d in (64, 128) else 1 << 30
     return lib.fa_decode_paged(q, kc, vc, pt, sl, page_size, o, lse, S, H, Hkv, d, num_pages,
                                max_pages, max_seq_len, scale, ws, ws_bytes, None)
@@ -156,7 +156,7 @@ def test_kv_append_validation(lib, kw, want):
 
 
 def test_decode_fp8_validation(lib):
-    ws = lib.fa_decode_paged_workspace_size(4, 32, 8, 128, 128, 16)
+    ws = lib.fa_decode_paged_workspace_size(4, 32, 128, 128, 16)
 
     def call(ks=P, vs=P, **kw):
         a = dict(q=P, kc=P, vc=P, pt=P, sl=P, page_size=16, o=P, lse=None, S=4, H=32, Hkv=8,
@@ -172,6 +172,18 @@ def test_decode_fp8_validation(lib):
     assert call(S=0) == INVALID
     assert call(d=96) == UNSUPPORTED
     assert call(H=32, Hkv=5) == INVALID
+
+
+def test_decode_cache_type_travels_with_scales(lib):
+    """The cache's element type is tied to its scale arrays: fa_decode_paged (bf16 cache)
+    takes none, fa_decode_paged_fp8 (e4m3 cache) needs both, and a call with only one of
+    them is rejected before anything is enqueued."""
+    assert len(_lib.SIGNATURES["fa_decode_paged"][1]) == 19
+    assert len(_lib.SIGNATURES["fa_decode_paged_fp8"][1]) == 21
+    ws = lib.fa_decode_paged_workspace_size(4, 32, 128, 128, 16)
+    for ks, vs in ((None, P), (P, None), (None, None)):
+        assert lib.fa_decode_paged_fp8(P, P, P, ks, vs, P, P, 16, P, None, 4, 32, 8, 128, 100,
+                                       8, 128, 0.09, P, ws, None) == INVALID
 
 
 def test_bwd_validation(lib):
@@ -194,23 +206,24 @@ def test_bwd_validation(lib):
 
 def test_workspace_size(lib):
     f = lib.fa_decode_paged_workspace_size
-    assert f(64, 32, 8, 128, 8192, 16) > 0
-    assert f(0, 32, 8, 128, 8192, 16) == 0
-    assert f(64, 32, 8, 100, 8192, 16) == 0
-    assert f(64, 32, 8, 128, 8192, 8) == 0
+    assert f(64, 32, 128, 8192, 16) > 0
+    assert f(0, 32, 128, 8192, 16) == 0
+    assert f(64, 32, 100, 8192, 16) == 0
+    assert f(64, 32, 128, 8192, 8) == 0
+    assert f(64, 0, 128, 8192, 16) == 0
     # fewest cached tokens a work-group's range holds: 4 pages, or 1/32 of the longest
     # possible sequence, at most 248 pages (62 per wave)
-    T = lib.fa_decode_paged_split_tokens(64, 8, 8192, 16)
+    T = lib.fa_decode_paged_split_tokens(64, 8192, 16)
     assert T == 16 * 16
     slots = -(-8192 // T) + 1  # segments a sequence can be cut into
     # partial results, per sequence its slot count, then the plan: 4 totals and 2 ints per
     # work-group row (at most max(1536, work-groups the longest cache needs, sequences))
     rows = max(1536, -(-(64 * 512) // 248), 64)
-    assert f(64, 32, 8, 128, 8192, 16) == (64 * 32 * slots * (128 + 1) * 4 + 64 * 4
+    assert f(64, 32, 128, 8192, 16) == (64 * 32 * slots * (128 + 1) * 4 + 64 * 4
                                            + (4 + 2 * rows) * 4)
-    assert lib.fa_decode_paged_split_tokens(1, 1, 100, 16) == 4 * 16
-    assert lib.fa_decode_paged_split_tokens(1, 1, 131072, 16) == 248 * 16
-    assert lib.fa_decode_paged_split_tokens(1, 1, 1 << 30, 16) == 248 * 16
+    assert lib.fa_decode_paged_split_tokens(1, 100, 16) == 4 * 16
+    assert lib.fa_decode_paged_split_tokens(1, 131072, 16) == 248 * 16
+    assert lib.fa_decode_paged_split_tokens(1, 1 << 30, 16) == 248 * 16
 
 
 def test_binding_refuses_host_tensors():

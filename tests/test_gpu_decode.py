@@ -64,7 +64,7 @@ def test_decode_long_ranges():
     page ids fill lanes 0-61 and the two pages it prefetches past its last one lanes
     62-63); the long sequence spans 34 ranges, the others begin and end inside ranges."""
     from kv_cache_fa_amd import _lib
-    assert _lib.fa_decode_paged_split_tokens(3, 1, 131072, 16) == 248 * 16
+    assert _lib.fa_decode_paged_split_tokens(3, 131072, 16) == 248 * 16
     cfg = inputs.DecodeConfig("long", 3, 4, 1, 64, 0, 0, 16, 131072, 1 / 8, 5)
     inp = inputs.make_decode(cfg, seq_lens=[131072, 4000, 70001])
     _check(inp, "decode long ranges")

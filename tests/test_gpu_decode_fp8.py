@@ -35,9 +35,8 @@ def run_fp8(f: inputs.DecodeFp8Inputs):
     sl = torch.from_numpy(b.seq_lens).cuda()
     o = torch.empty_like(q)
     lse = torch.empty((c.num_seqs, c.H), dtype=torch.float32, device="cuda")
-    ws = torch.empty(_lib.fa_decode_paged_workspace_size(c.num_seqs, c.H, c.Hkv, c.d,
-                                                         c.max_seq_len), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(_lib.fa_decode_paged_workspace_size(c.num_seqs, c.H, c.d, c.max_seq_len),
+                     dtype=torch.uint8, device="cuda")
     _lib.fa_decode_paged_fp8(q, kc, vc, ks, vs, pt, sl, o, lse, max_seq_len=c.max_seq_len,
                              scale=c.scale, workspace=ws)
     torch.cuda.synchronize()
@@ -104,11 +103,14 @@ def test_fp8_decode_pairs_with_padding_columns():
     _check(inputs.quantize_decode_fp8(base), "fp8 pairs g=2")
 
 
-def test_fp8_edge_lengths_and_nan_slots():
+@pytest.mark.parametrize("S", [8, 40])
+def test_fp8_edge_lengths_and_nan_slots(S):
     """Empty sequence, page boundaries; unused slots hold e4m3 NaN bytes and the table is
-    padded with -1: the output must equal the zero-filled cache's bit for bit."""
-    cfg = inputs.DecodeConfig("edges", 8, 8, 2, 128, 0, 0, 16, 600, 1 / math.sqrt(128), 3)
-    lens = [0, 1, 15, 16, 17, 64, 65, 600]
+    padded with -1: the output must equal the zero-filled cache's bit for bit. 8 sequences
+    take the one-KV-head kernel; 40 (H8 Hkv2, g = 4) the kernel that reads two KV heads'
+    rows as one."""
+    cfg = inputs.DecodeConfig("edges", S, 8, 2, 128, 0, 0, 16, 600, 1 / math.sqrt(128), 3)
+    lens = ([0, 1, 15, 16, 17, 64, 65, 600] * (S // 8))[:S]
     a = inputs.quantize_decode_fp8(inputs.make_decode(cfg, seq_lens=lens))
     b = inputs.quantize_decode_fp8(inputs.make_decode(cfg, seq_lens=lens, unused_fill="nan",
                                                       table_pad=-1))

@@ -276,7 +276,7 @@ def test_prefill_append_decode_flow():
             pos += n
 
     # decode steps for all sequences at once
-    ws = torch.empty(_lib.fa_decode_paged_workspace_size(S, H, Hkv, d, max_len),
+    ws = torch.empty(_lib.fa_decode_paged_workspace_size(S, H, d, max_len),
                      dtype=torch.uint8, device="cuda")
     for t in range(steps):
         _say(f"[flow] decode step {t}")
