@@ -78,16 +78,49 @@ def decode_flops(inp: inputs.DecodeInputs) -> float:
     return 4.0 * inp.cfg.d * inp.cfg.H * float(inp.seq_lens.astype(np.int64).sum())
 
 
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_small(name: str):
+    """The fp64 oracle on a whole small prefill workload (every row), timed."""
+    import oracle  # test infrastructure, used only for the baseline legs
+    c = inputs.PREFILL_CONFIGS[name]
+    q, k, v = inputs.make_prefill(c).as_f64()
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, causal=c.causal, scale=c.scale)
+    t = time.perf_counter() - t0
+    return {"s": round(t, 4), "GFLOP/s": round(c.flops / t / 1e9, 3), "cores": blas_threads(),
+            "sample": f"the whole {name} workload (all {c.B * c.H * c.Nq} rows), fp64 NumPy"}
+
+
+def cpu_baseline_decode(dinp: inputs.DecodeInputs, d_bytes: int):
+    """The fp64 oracle on the whole paged-decode workload (all sequences and heads, from
+    each sequence's contiguous K/V), timed; rate in the decode metric's unit."""
+    import oracle  # test infrastructure, used only for the baseline legs
+    q = inputs.bf16_bits_to_f64(dinp.q)
+    ks = [inputs.bf16_bits_to_f64(x) for x in dinp.k_seq]
+    vs = [inputs.bf16_bits_to_f64(x) for x in dinp.v_seq]
+    t0 = time.perf_counter()
+    oracle.decode(q, ks, vs, scale=dinp.cfg.scale)
+    t = time.perf_counter() - t0
+    return {"value": round(d_bytes / t / 1e9, 3), "unit": "GB/s", "cores": blas_threads(),
+            "kind": "oracle", "s": round(t, 3),
+            "sample": f"the whole paged_decode workload ({dinp.cfg.num_seqs} sequences x "
+                      f"{dinp.cfg.H} heads, {int(dinp.seq_lens.sum())} cached tokens), fp64 "
+                      "NumPy; rate = the call's algorithmic bytes / oracle time"}
+
+
 def cpu_baseline(pinp: inputs.PrefillInputs, budget_s: float = 12.0):
     """The fp64 oracle (as it stands) on a bounded sample of the prefill workload:
     random query rows of head 0, each against its full causal prefix."""
     import oracle  # test infrastructure, used only for this baseline leg
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()
-                     if i.get("user_api") == "blas"] or [1])
-    except Exception:  # noqa: BLE001
-        cores = len(os.sched_getaffinity(0))
+    cores = blas_threads()
     c = pinp.cfg
     q = inputs.bf16_bits_to_f64(pinp.q[:1, :1])
     k = inputs.bf16_bits_to_f64(pinp.k[:1, :1])
@@ -318,8 +351,7 @@ def main(argv=None):
         # dP, dQ, dK and the recomputed S: 5 products of 2d flops per attending pair); the
         # kernels execute 7 (S and dP are computed again for dQ).
         log("[bench] extra: gqa_causal backward")
-        gdo = torch.randn(gq.shape, generator=torch.Generator(device=dev).manual_seed(5),
-                          device=dev).to(torch.bfloat16)
+        gdo = to_dev(inputs.make_dout(gcfg, seed=gcfg.seed + 100))
         gdq, gdk, gdv = torch.empty_like(gq), torch.empty_like(gk), torch.empty_like(gv)
         gws = torch.empty(_lib.fa_bwd_workspace_size(gcfg.B, gcfg.H, gcfg.Nq), dtype=torch.uint8,
                           device=dev)
@@ -361,19 +393,20 @@ def main(argv=None):
 
         # Sliding-window prefill: B1 H32 Hkv8 N32768 d128, causal window of 4096 keys.
         log("[bench] extra: sliding-window prefill")
-        wB, wH, wHkv, wN, wd, wl = 1, 32, 8, 32768, 128, 4096
-        gen = torch.Generator(device=dev).manual_seed(777)
-        wq = torch.randn((wB, wH, wN, wd), generator=gen, device=dev).to(torch.bfloat16)
-        wk = torch.randn((wB, wHkv, wN, wd), generator=gen, device=dev).to(torch.bfloat16)
-        wv = torch.randn((wB, wHkv, wN, wd), generator=gen, device=dev).to(torch.bfloat16)
+        wcfg = inputs.WINDOW_CONFIG
+        wB, wH, wHkv, wN, wd = wcfg.B, wcfg.H, wcfg.Hkv, wcfg.Nq, wcfg.d
+        wl, wr = inputs.WINDOW
+        winp = inputs.make_prefill(wcfg)
+        wq, wk, wv = to_dev(winp.q), to_dev(winp.k), to_dev(winp.v)
+        del winp
         wo = torch.empty_like(wq)
         wlse = torch.empty((wB, wH, wN), dtype=torch.float32, device=dev)
         w_ms = timed(lambda: _lib.fa_fwd_window(wq, wk, wv, wo, wlse, window_left=wl,
-                                                window_right=0, scale=wd ** -0.5, stream=stream))
-        w_flops = 4.0 * wd * wB * wH * inputs.window_pairs(wN, wN, wl, 0)
+                                                window_right=wr, scale=wcfg.scale, stream=stream))
+        w_flops = 4.0 * wd * wB * wH * inputs.window_pairs(wN, wN, wl, wr)
         w_tf = w_flops / (w_ms * 1e-3) / 1e12
         out["legs"]["prefill_sliding_window"] = {
-            "B": wB, "H": wH, "Hkv": wHkv, "N": wN, "d": wd, "window": [wl, 0],
+            "B": wB, "H": wH, "Hkv": wHkv, "N": wN, "d": wd, "window": [wl, wr],
             "flops": w_flops, "ms_mean": round(w_ms, 4), "TFLOP/s": round(w_tf, 2),
             "frac_of_bf16_peak": round(w_tf / PEAK_BF16_TFLOPS, 4)}
         del wq, wk, wv, wo, wlse
@@ -426,6 +459,13 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle sample)")
         out["cpu_baseline"] = cpu_baseline(pinp)
+        log("[bench] cpu baseline (oracle, whole decode workload)")
+        dec = cpu_baseline_decode(dinp, d_bytes)
+        out["cpu_baseline"]["decode"] = dec
+        out["legs"]["decode"]["cpu_baseline"] = dec
+        log("[bench] cpu baseline (oracle, whole small prefill workloads)")
+        for name in ("fp32_single", "bf16_causal"):
+            out["cpu_baseline"][name] = cpu_baseline_small(name)
 
     print(json.dumps(out))
     return 0

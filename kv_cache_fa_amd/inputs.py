@@ -16,6 +16,9 @@ head; the KV-cache and GQA structure follows the glossary entry "KV Cache
   paged_decode  64 sequences x 1 query, H=32 Hkv=8 d=128, KV length ~ U{512..8192},
                 pages of 16 tokens, seeded random permutation page table
   long_causal   B=1 H=8  Hkv=8 N=131072 d=128 causal bf16, N(0,1) x 0.5
+  window_long   B=1 H=32 Hkv=8 N=32768  d=128 bf16, N(0,1), sliding window (4096, 0)
+
+The backward pass's output gradient dO is drawn from its own generator (make_dout).
 
 Draw order for a prefill workload (one ``numpy.random.default_rng(seed)``):
 Q, K, V, each ``standard_normal(dtype=float32)`` in [B, H(kv), N, d] order, then
@@ -179,6 +182,12 @@ PREFILL_CONFIGS = {
                                  0.5, 1.0 / math.sqrt(128), 5),
 }
 
+# The sliding-window workload: B1 H32 Hkv8 N32768 d128 with a causal window of 4096 keys
+# (each query attends its own position and the 4096 before it).
+WINDOW_CONFIG = PrefillConfig("window_long", 1, 32, 8, 32768, 32768, 128, False, "bf16",
+                              1.0, 1.0 / math.sqrt(128), 6)
+WINDOW = (4096, 0)
+
 DECODE_CONFIGS = {
     "paged_decode": DecodeConfig("paged_decode", 64, 32, 8, 128, 512, 8192, 16, 8192,
                                  1.0 / math.sqrt(128), 4),
@@ -228,6 +237,14 @@ def custom_prefill(B, H, Hkv, Nq, Nk, d, causal, dtype="bf16", value_scale=1.0,
         scale = 1.0 / math.sqrt(d)
     cfg = PrefillConfig(name, B, H, Hkv, Nq, Nk, d, causal, dtype, value_scale, scale, seed)
     return make_prefill(cfg)
+
+
+def make_dout(cfg: PrefillConfig, seed: int) -> np.ndarray:
+    """Output gradient dO [B,H,Nq,d] for the backward pass: N(0,1) float32 draws from
+    default_rng(seed), rounded to bf16 (bits)."""
+    rng = np.random.default_rng(seed)
+    return f32_to_bf16_bits(rng.standard_normal((cfg.B, cfg.H, cfg.Nq, cfg.d),
+                                                dtype=np.float32))
 
 
 def sample_rows(inp: PrefillInputs, n_full_pairs: int, n_random_rows: int):

@@ -95,3 +95,32 @@ def test_backward_deterministic():
     b = run_bwd(inp, do)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_backward_gqa_causal_workload_sampled_groups():
+    """The benched backward workload, B4 H32 Hkv8 N4096 d128 causal (the GQA causal
+    prefill's inputs, dO from inputs.make_dout): the kernels run on the whole workload and
+    two seeded (batch, KV head) groups are compared in full with the oracle: dK and dV of
+    the group's KV head and dQ of its g = 4 query heads."""
+    import torch
+    cfg = inputs.PREFILL_CONFIGS["gqa_causal"]
+    inp = inputs.make_prefill(cfg)
+    do_bits = inputs.make_dout(cfg, seed=cfg.seed + 100)
+    _say(f"[bwd] {cfg.name} full workload")
+    dq, dk, dv = run_bwd(inp, do_bits)
+    torch.cuda.empty_cache()
+    g = cfg.H // cfg.Hkv
+    rng = np.random.default_rng(31)
+    picks = rng.choice(cfg.B * cfg.Hkv, size=2, replace=False)
+    for p in sorted(int(x) for x in picks):
+        b, kvh = p // cfg.Hkv, p % cfg.Hkv
+        hs = slice(kvh * g, (kvh + 1) * g)
+        _say(f"[bwd] oracle group b={b} kv head {kvh}")
+        q = inputs.bf16_bits_to_f64(inp.q[b:b + 1, hs])
+        k = inputs.bf16_bits_to_f64(inp.k[b:b + 1, kvh:kvh + 1])
+        v = inputs.bf16_bits_to_f64(inp.v[b:b + 1, kvh:kvh + 1])
+        do = inputs.bf16_bits_to_f64(do_bits[b:b + 1, hs])
+        rq, rk, rv = oracle.attention_backward(q, k, v, do, causal=True, scale=cfg.scale)
+        check_grad(dq[b:b + 1, hs], rq, f"dQ b{b} heads {hs.start}..{hs.stop - 1}")
+        check_grad(dk[b:b + 1, kvh:kvh + 1], rk, f"dK b{b} kv{kvh}")
+        check_grad(dv[b:b + 1, kvh:kvh + 1], rv, f"dV b{b} kv{kvh}")

@@ -99,3 +99,28 @@ def test_window_long_gqa_sampled():
     gl = np.concatenate([lse_h[b, h, idx] for (b, h), idx in rows.items()])
     wl = np.concatenate([L[key] for key in rows])
     check_bf16(got, gl, want, wl, "window long GQA")
+
+
+def test_window_benched_workload_sampled():
+    """The benched sliding-window workload (inputs.WINDOW_CONFIG: B1 H32 Hkv8 N32768 d128,
+    window (4096, 0)): 256 seeded rows in each of 4 heads, plus the rows at the window's
+    edges (the last row whose window still reaches key 0, the first that does not, their
+    neighbours, the first and last rows)."""
+    cfg = inputs.WINDOW_CONFIG
+    left, right = inputs.WINDOW
+    inp = inputs.make_prefill(cfg)
+    _say(f"[window] {cfg.name} ({left},{right}) sampled")
+    o_h, lse_h = run_window(inp, left, right)
+    rng = np.random.default_rng(12)
+    edges = np.array([0, 1, left - 1, left, left + 1, 2 * left, cfg.Nq - 2, cfg.Nq - 1])
+    heads = rng.choice(cfg.H, size=4, replace=False)
+    rows = {(0, int(h)): np.unique(np.concatenate([edges, rng.choice(cfg.Nq, 256, replace=False)]))
+            for h in sorted(heads)}
+    q, k, v = inp.as_f64()
+    O, L = oracle.attention(q, k, v, causal=False, scale=cfg.scale, rows=rows,
+                            window=(left, right))
+    got = np.concatenate([inputs.bf16_bits_to_f64(o_h[b, h, idx]) for (b, h), idx in rows.items()])
+    want = np.concatenate([O[key] for key in rows])
+    gl = np.concatenate([lse_h[b, h, idx] for (b, h), idx in rows.items()])
+    wl = np.concatenate([L[key] for key in rows])
+    check_bf16(got, gl, want, wl, "window benched workload")
