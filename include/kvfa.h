@@ -48,7 +48,8 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID = -1,      /* an argument is out of its documented range           */
     FA_ERR_UNSUPPORTED = -2,  /* a valid request this build does not implement        */
-    FA_ERR_HIP = -3           /* the HIP runtime reported an error at launch          */
+    FA_ERR_HIP = -3,          /* the HIP runtime reported an error at launch          */
+    FA_ERR_SCRATCH = -4       /* fa_decode_paged_noalloc: request exceeds its scratch */
 } fa_status;
 
 /*
@@ -188,6 +189,31 @@ int fa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
                         void* o, float* lse, int num_seqs, int H, int Hkv, int d,
                         int num_pages, int max_pages_per_seq, int max_seq_len, float scale,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_decode_paged_noalloc — fa_decode_paged for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It takes no workspace argument: the decode workspace lives in a static
+ * device array of FA_NOALLOC_SCRATCH_BYTES, one per GPU the library runs on, held until
+ * the process ends. The call itself allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); its first call on a device looks up that device's array
+ * address once.
+ * Arguments, layouts, numerics, device-side behaviour and errors are those of
+ * fa_decode_paged (same kernels, same results bit for bit), except that a call whose
+ * workspace, fa_decode_paged_workspace_size(num_seqs, H, d, max_seq_len, page_size),
+ * would exceed FA_NOALLOC_SCRATCH_BYTES returns FA_ERR_SCRATCH before anything is
+ * enqueued (the 64-sequence, H32, d 128, 8192-token decode needs about 35 MB).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams or from different threads) race and must be serialised by the
+ * caller. Calls in order on one stream are safe.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+int fa_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* page_table, const int32_t* seq_lens, int page_size,
+                            void* o, float* lse, int num_seqs, int H, int Hkv, int d,
+                            int num_pages, int max_pages_per_seq, int max_seq_len, float scale,
+                            hipStream_t stream);
 
 /* The fewest cached tokens one split-K work-group's range holds for these sizes (a
  * multiple of the page size: 4 pages, or 1/32 of max_seq_len's pages, at most 248 pages).

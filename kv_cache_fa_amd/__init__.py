@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     fa_bwd_workspace_size,
     fa_decode_paged,
     fa_decode_paged_fp8,
+    fa_decode_paged_noalloc,
     fa_decode_paged_split_tokens,
     fa_decode_paged_workspace_size,
     fa_fwd,

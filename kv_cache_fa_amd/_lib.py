@@ -14,7 +14,9 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvfa.so")
 
-FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_SCRATCH = 0, -1, -2, -3, -4
+# Size of the static device array behind fa_decode_paged_noalloc (kvfa.h)
+FA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -26,6 +28,8 @@ SIGNATURES = {
     "fa_decode_paged_split_tokens": (_i, [_i, _i, _i]),
     "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                              _f, _vp, _sz, _vp]),
+    "fa_decode_paged_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i,
+                                     _i, _i, _f, _vp]),
     "fa_fwd_two_pass": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp]),
     "fa_fwd_window": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp]),
     "fa_fwd_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
@@ -205,6 +209,30 @@ def fa_decode_paged(q, k_cache, v_cache, page_table, seq_lens, o, lse=None, *, m
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), page_size,
         _ptr(o), _ptr(lse), S, H, Hkv, d, num_pages, int(page_table.shape[1]), int(max_seq_len),
         float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def fa_decode_paged_noalloc(q, k_cache, v_cache, page_table, seq_lens, o, lse=None, *,
+                            max_seq_len: int, scale: float, stream=None):
+    """Paged decode with the workspace in the library's static device array (no
+    allocation anywhere in the call). Same tensors as fa_decode_paged, no workspace."""
+    import torch
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (o, "o")):
+        _check_tensor(t, torch.bfloat16, n)
+    _check_tensor(page_table, torch.int32, "page_table")
+    _check_tensor(seq_lens, torch.int32, "seq_lens")
+    S, H, d = q.shape
+    num_pages, page_size, Hkv, dk = k_cache.shape
+    _require(dk == d and tuple(v_cache.shape) == tuple(k_cache.shape), "cache shape mismatch")
+    _require(tuple(o.shape) == tuple(q.shape), "o must have q's shape")
+    _require(page_table.dim() == 2 and page_table.shape[0] == S, "page_table must be [S, M]")
+    _require(tuple(seq_lens.shape) == (S,), "seq_lens must be [S]")
+    if lse is not None:
+        _check_tensor(lse, torch.float32, "lse")
+        _require(tuple(lse.shape) == (S, H), "lse must be [S,H]")
+    _check("fa_decode_paged_noalloc", lib().fa_decode_paged_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), page_size,
+        _ptr(o), _ptr(lse), S, H, Hkv, d, num_pages, int(page_table.shape[1]), int(max_seq_len),
+        float(scale), _stream(stream)))
 
 
 def fa_fwd_paged(q, k_cache, v_cache, page_table, seq_lens, o, lse=None, *, max_seq_len: int,

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "kvfa.h"
 #include "launch.h"
 
@@ -129,16 +131,14 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
 }  // extern "C"
 
 namespace {
-int decode_checked(const void* q, const void* k_cache, const void* v_cache,
-                   const int32_t* page_table, const int32_t* seq_lens, int page_size, void* o,
-                   float* lse, int num_seqs, int H, int Hkv, int d, int num_pages,
-                   int max_pages_per_seq, int max_seq_len, float scale, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream, const float* k_scale,
-                   const float* v_scale) {
-    if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !o || !workspace)
-        return FA_ERR_INVALID;
+// Checks of the decode arguments other than the workspace (host only, no HIP call).
+int decode_args_status(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* page_table, const int32_t* seq_lens, int page_size,
+                       void* o, float* lse, int num_seqs, int H, int Hkv, int d,
+                       int num_pages, int max_pages_per_seq, int max_seq_len, float scale) {
+    if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !o) return FA_ERR_INVALID;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
-        !aligned(workspace, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4))
+        !aligned(page_table, 4) || !aligned(seq_lens, 4))
         return FA_ERR_INVALID;
     if (lse && !aligned(lse, 4)) return FA_ERR_INVALID;
     if (num_seqs < 1 || H < 1 || Hkv < 1 || num_pages < 1 || max_pages_per_seq < 1 ||
@@ -156,6 +156,20 @@ int decode_checked(const void* q, const void* k_cache, const void* v_cache,
     if ((long long)num_seqs * ((max_seq_len + page_size - 1) / page_size) >= (1LL << 30) ||
         kvfa::decode_min_work_groups(num_seqs, max_seq_len) > 65535)
         return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+int decode_checked(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* page_table, const int32_t* seq_lens, int page_size, void* o,
+                   float* lse, int num_seqs, int H, int Hkv, int d, int num_pages,
+                   int max_pages_per_seq, int max_seq_len, float scale, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream, const float* k_scale,
+                   const float* v_scale) {
+    const int st = decode_args_status(q, k_cache, v_cache, page_table, seq_lens, page_size, o,
+                                      lse, num_seqs, H, Hkv, d, num_pages, max_pages_per_seq,
+                                      max_seq_len, scale);
+    if (st != FA_OK) return st;
+    if (!workspace || !aligned(workspace, 16)) return FA_ERR_INVALID;
     if (workspace_bytes < kvfa::decode_workspace_bytes(num_seqs, H, d, max_seq_len))
         return FA_ERR_INVALID;
     // The cache type travels with the scales: an e4m3 cache has both, a bf16 one neither.
@@ -257,6 +271,9 @@ int fa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
 const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "FA_OK";
+        case FA_ERR_SCRATCH:
+            return "FA_ERR_SCRATCH: the call needs more workspace than the static scratch of "
+                   "fa_decode_paged_noalloc (FA_NOALLOC_SCRATCH_BYTES)";
         case FA_ERR_INVALID: return "FA_ERR_INVALID: an argument is out of its documented range";
         case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: valid request not implemented";
         case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
@@ -265,3 +282,59 @@ const char* fa_status_string(int status) {
 }
 
 }  // extern "C"
+
+// ---- fa_decode_paged_noalloc: the decode workspace in a static device array ----------
+// `scratch` exists once per GPU the library runs on (the code object's globals are
+// placed on each device when the library's kernels load there) and is kept until the
+// process ends. In host code its name is only a stand-in: the device address is looked
+// up once per device with hipGetSymbolAddress, with that device current, and that
+// address is what the kernels receive. Every call on a device shares the device's
+// array, so calls that overlap on one GPU (different streams, or threads) race.
+namespace {
+__device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];  // device address of `scratch`, per device id
+
+// Device address of the current device's `scratch` (looked up on its first use there).
+int scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "fa_decode_paged_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "fa_decode_paged_noalloc: hipGetSymbolAddress");
+        if (p == nullptr) return FA_ERR_HIP;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return FA_OK;
+}
+}  // namespace
+
+extern "C" int fa_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* page_table, const int32_t* seq_lens,
+                                       int page_size, void* o, float* lse, int num_seqs, int H,
+                                       int Hkv, int d, int num_pages, int max_pages_per_seq,
+                                       int max_seq_len, float scale, hipStream_t stream) {
+    const int st = decode_args_status(q, k_cache, v_cache, page_table, seq_lens, page_size, o,
+                                      lse, num_seqs, H, Hkv, d, num_pages, max_pages_per_seq,
+                                      max_seq_len, scale);
+    if (st != FA_OK) return st;
+    const size_t need = kvfa::decode_workspace_bytes(num_seqs, H, d, max_seq_len);
+    if (need > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+    void* ws = nullptr;
+    const int sst = scratch_address(&ws);
+    if (sst != FA_OK) return sst;
+    // Nothing in the workspace has to start at zero: each word a decode call reads was
+    // written earlier in the same call (slot counts, partial results, the range plan).
+    hipError_t e = kvfa::launch_decode_paged(q, k_cache, v_cache, page_table, seq_lens, o, lse,
+                                             num_seqs, H, Hkv, d, num_pages, max_pages_per_seq,
+                                             max_seq_len, scale, ws, stream,
+                                             kvfa::DecodeCache::kBf16, nullptr, nullptr);
+    return hip_status(e, "fa_decode_paged_noalloc");
+}

@@ -35,7 +35,8 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert set(declared_functions()) == {
         "fa_fwd", "fa_fwd_fp32", "fa_decode_paged", "fa_decode_paged_workspace_size",
-        "fa_decode_paged_split_tokens", "fa_fwd_paged", "fa_kv_append", "fa_fwd_window", "fa_fwd_two_pass", "fa_decode_paged_fp8", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string"}
+        "fa_decode_paged_split_tokens", "fa_fwd_paged", "fa_kv_append", "fa_fwd_window", "fa_fwd_two_pass", "fa_decode_paged_fp8", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string",
+        "fa_decode_paged_noalloc"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -45,8 +46,9 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for st in (0, -1, -2, -3, 7):
+    for st in (0, -1, -2, -3, -4, 7):
         assert _lib.fa_status_string(st)
+    assert _lib.fa_status_string(-4).startswith("FA_ERR_SCRATCH")
     assert _lib.fa_status_string(-1).startswith("FA_ERR_INVALID")
 
 
@@ -184,6 +186,25 @@ def test_decode_cache_type_travels_with_scales(lib):
     for ks, vs in ((None, P), (P, None), (None, None)):
         assert lib.fa_decode_paged_fp8(P, P, P, ks, vs, P, P, 16, P, None, 4, 32, 8, 128, 100,
                                        8, 128, 0.09, P, ws, None) == INVALID
+
+
+def test_decode_noalloc_host_checks(lib):
+    """The no-allocation decode checks its arguments like fa_decode_paged and refuses a
+    workspace need beyond its static array, all before any HIP call."""
+    def call(S=4, H=32, Hkv=8, d=128, max_pages=8, max_seq_len=128, q=P, pt=P, scale=0.09):
+        return lib.fa_decode_paged_noalloc(q, P, P, pt, P, 16, P, None, S, H, Hkv, d, 100,
+                                           max_pages, max_seq_len, scale, None)
+    assert call(q=None) == INVALID
+    assert call(pt=P + 2) == INVALID
+    assert call(H=32, Hkv=5) == INVALID
+    assert call(scale=0.0) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    S, L = 256, 8192
+    assert lib.fa_decode_paged_workspace_size(S, 32, 128, L, 16) > _lib.FA_NOALLOC_SCRATCH_BYTES
+    assert call(S=S, max_pages=L // 16, max_seq_len=L) == _lib.FA_ERR_SCRATCH
+    # the 64-sequence, 8192-token decode workload fits
+    assert lib.fa_decode_paged_workspace_size(64, 32, 128, 8192, 16) <= \
+        _lib.FA_NOALLOC_SCRATCH_BYTES
 
 
 def test_bwd_validation(lib):
