@@ -35,9 +35,21 @@ METRIC = "prefill attn TFLOP/s (bf16 causal) + decode KV GB/s, % of MI355X peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = {
-    "fwd_pp_kernel": os.path.join(ROOT, "kv_cache_fa_amd", "csrc", "prefill_pp.hip"),
-    "decode_split_kernel": os.path.join(ROOT, "kv_cache_fa_amd", "csrc", "decode.hip"),
+CSRC = os.path.join(ROOT, "kv_cache_fa_amd", "csrc")
+# The sources each leg's kernels are built from (their hash dates the counter runs).
+_COMMON = ["common.h", "launch.h"]
+LEG_SOURCES = {
+    "prefill": ["prefill_pp.hip", "prefill_ks.hip", "prefill_common.h"] + _COMMON,
+    "prefill_gqa_causal": ["prefill_pp.hip", "prefill_ks.hip", "prefill_common.h"] + _COMMON,
+    "prefill_small_causal": ["prefill_pp.hip", "prefill_ks.hip", "prefill_common.h"] + _COMMON,
+    "chunked_prefill_paged": ["prefill_pp.hip", "prefill_common.h"] + _COMMON,
+    "prefill_sliding_window": ["prefill_pp.hip", "prefill_common.h"] + _COMMON,
+    "prefill_gqa_causal_two_pass": ["prefill_bf16.hip", "prefill_common.h"] + _COMMON,
+    "backward_gqa_causal": ["backward.hip", "prefill_common.h"] + _COMMON,
+    "decode": ["decode.hip"] + _COMMON,
+    "decode_fp8": ["decode.hip"] + _COMMON,
+    "decode_g16": ["decode.hip"] + _COMMON,
+    "kv_append": ["kv_append.hip"] + _COMMON,
 }
 
 
@@ -45,24 +57,28 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_sha(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(files) -> str:
+    h = hashlib.sha256()
+    for name in files:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed counter runs, if they still describe
-    the current kernel source (else None)."""
+def measured_traffic(leg: str, workload: str):
+    """HBM bytes per call of a leg from the committed counter runs (FETCH_SIZE +
+    WRITE_SIZE, each scaled by its reading for a device copy of known size), if they
+    still describe the current kernel sources (else None)."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(kernel)
+            rec = json.load(f).get(leg)
     except (OSError, ValueError):
         return None
     if not rec or rec.get("workload") != workload:
         return None
-    if rec.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+    if rec.get("source_sha") != source_sha(LEG_SOURCES[leg]):
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("bytes_per_call")
 
 
 def decode_bytes(inp: inputs.DecodeInputs) -> int:
@@ -155,6 +171,10 @@ def main(argv=None):
                     help="skip the separately timed GQA prefill measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--reps", type=int, default=20,
+                    help="timed calls per extra leg (the small prefill leg takes 5x)")
+    ap.add_argument("--warm-s", type=float, default=0.2,
+                    help="warm-up seconds before each extra leg (0: none; for profiling)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -235,8 +255,8 @@ def main(argv=None):
     p_tflops = p_flops / (p_ms.mean() * 1e-3) / 1e12
     d_gbs = d_bytes / (d_ms.mean() * 1e-3) / 1e9
 
-    p_traffic = measured_traffic("fwd_pp_kernel", pcfg.name)
-    d_traffic = measured_traffic("decode_split_kernel", dcfg.name)
+    p_traffic = measured_traffic("prefill", pcfg.name)
+    d_traffic = measured_traffic("decode", dcfg.name)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -291,11 +311,12 @@ def main(argv=None):
         "wall_s_timed": round(t_wall, 3),
     }
 
-    def timed(fn, n=20, warm_s=0.2):
-        """Mean ms of fn over n back-to-back launches, after ~warm_s of warm-up (the
+    def timed(fn, n=None):
+        """Mean ms of fn over n back-to-back launches, after ~--warm-s of warm-up (the
         clock ramps up under sustained load)."""
+        n = args.reps if n is None else n
         w0 = time.perf_counter()
-        while time.perf_counter() - w0 < warm_s:
+        while time.perf_counter() - w0 < args.warm_s:
             for _ in range(n):
                 fn()
             torch.cuda.synchronize()
@@ -320,7 +341,8 @@ def main(argv=None):
         out["legs"]["prefill_gqa_causal"] = {
             "B": gcfg.B, "H": gcfg.H, "Hkv": gcfg.Hkv, "N": gcfg.Nq, "d": gcfg.d,
             "ms_mean": round(g_ms, 4), "TFLOP/s": round(g_tf, 2),
-            "frac_of_bf16_peak": round(g_tf / PEAK_BF16_TFLOPS, 4)}
+            "frac_of_bf16_peak": round(g_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic("prefill_gqa_causal", gcfg.name)}
         # The small causal case (B2 H8 N1024 d64): a few microseconds, so launch-bound;
         # reported, not a target.
         scfg = inputs.PREFILL_CONFIGS["bf16_causal"]
@@ -330,12 +352,13 @@ def main(argv=None):
         so = torch.empty_like(sq)
         slse = torch.empty((scfg.B, scfg.H, scfg.Nq), dtype=torch.float32, device=dev)
         s_ms = timed(lambda: _lib.fa_fwd(sq, sk, sv, so, slse, causal=True, scale=scfg.scale,
-                                         stream=stream), n=100)
+                                         stream=stream), n=5 * args.reps)
         s_tf = scfg.flops / (s_ms * 1e-3) / 1e12
         out["legs"]["prefill_small_causal"] = {
             "B": scfg.B, "H": scfg.H, "Hkv": scfg.Hkv, "N": scfg.Nq, "d": scfg.d,
             "ms_mean": round(s_ms, 4), "TFLOP/s": round(s_tf, 2),
-            "frac_of_bf16_peak": round(s_tf / PEAK_BF16_TFLOPS, 4)}
+            "frac_of_bf16_peak": round(s_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic("prefill_small_causal", scfg.name)}
         del sq, sk, sv, so, slse
         # The same workload through the FlashAttention-1 two-pass path (statistics pass +
         # output pass); TFLOP/s counts the algorithmic flops, not the recomputed Q.K^T.
@@ -346,6 +369,7 @@ def main(argv=None):
         out["legs"]["prefill_gqa_causal_two_pass"] = {
             "ms_mean": round(t_ms, 4), "TFLOP/s": round(t_tf, 2),
             "frac_of_bf16_peak": round(t_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic("prefill_gqa_causal_two_pass", gcfg.name),
             "mfma_flops_executed_per_algorithmic": 1.5}
         # Backward pass on the same workload: algorithmic flops 2.5x the forward's (dV,
         # dP, dQ, dK and the recomputed S: 5 products of 2d flops per attending pair); the
@@ -362,6 +386,7 @@ def main(argv=None):
         out["legs"]["backward_gqa_causal"] = {
             "ms_mean": round(b_ms, 4), "TFLOP/s": round(b_tf, 2),
             "frac_of_bf16_peak": round(b_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic("backward_gqa_causal", gcfg.name),
             "flops": 2.5 * gcfg.flops, "mfma_flops_executed_per_algorithmic": 1.4}
         del gdo, gdq, gdk, gdv, gws
         del gq, gk, gv, go, glse
@@ -388,7 +413,8 @@ def main(argv=None):
             "B": B, "H": H, "Hkv": Hkv, "Nq": Nq, "d": d,
             "seq_lens": [int(x) for x in c.seq_lens], "flops": c_flops,
             "ms_mean": round(c_ms, 4), "TFLOP/s": round(c_tf, 2),
-            "frac_of_bf16_peak": round(c_tf / PEAK_BF16_TFLOPS, 4)}
+            "frac_of_bf16_peak": round(c_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic("chunked_prefill_paged", "chunked_prefill_paged")}
         del cq, ckc, cvc, co, clse
 
         # Sliding-window prefill: B1 H32 Hkv8 N32768 d128, causal window of 4096 keys.
@@ -408,7 +434,8 @@ def main(argv=None):
         out["legs"]["prefill_sliding_window"] = {
             "B": wB, "H": wH, "Hkv": wHkv, "N": wN, "d": wd, "window": [wl, wr],
             "flops": w_flops, "ms_mean": round(w_ms, 4), "TFLOP/s": round(w_tf, 2),
-            "frac_of_bf16_peak": round(w_tf / PEAK_BF16_TFLOPS, 4)}
+            "frac_of_bf16_peak": round(w_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic("prefill_sliding_window", wcfg.name)}
         del wq, wk, wv, wo, wlse
 
         # Paged decode on an fp8 (e4m3) copy of the decode workload's cache.
@@ -427,8 +454,37 @@ def main(argv=None):
         out["legs"]["decode_fp8"] = {
             "bytes": f_bytes, "ms_mean": round(f_ms, 4), "GB/s": round(f_gbs, 1),
             "frac_of_hbm_peak": round(f_gbs / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic("decode_fp8", "paged_decode"),
             "tokens_per_s": round(float(dinp.seq_lens.sum()) / (f_ms * 1e-3), 1)}
         del fkc, fvc, fks, fvs
+
+        # Paged decode with a wide GQA group: the decode workload's shape with two KV
+        # heads (H32 Hkv2, 16 query heads per KV head), lengths U{512..8192}.
+        log("[bench] extra: paged decode, 16 query heads per KV head")
+        ginp16 = inputs.custom_decode(dcfg.num_seqs, 32, 2, dcfg.d, dcfg.len_lo, dcfg.len_hi,
+                                      seed=dcfg.seed)
+        gq16 = to_dev(ginp16.q)
+        gkc16, gvc16 = to_dev(ginp16.k_cache), to_dev(ginp16.v_cache)
+        gpt16 = torch.from_numpy(ginp16.page_table).to(dev)
+        gsl16 = torch.from_numpy(ginp16.seq_lens).to(dev)
+        go16 = torch.empty_like(gq16)
+        glse16 = torch.empty((dcfg.num_seqs, 32), dtype=torch.float32, device=dev)
+        gws16 = torch.empty(_lib.fa_decode_paged_workspace_size(dcfg.num_seqs, 32, dcfg.d,
+                                                                 ginp16.cfg.max_seq_len),
+                            dtype=torch.uint8, device=dev)
+        g16_ms = timed(lambda: _lib.fa_decode_paged(gq16, gkc16, gvc16, gpt16, gsl16, go16,
+                                                     glse16, max_seq_len=ginp16.cfg.max_seq_len,
+                                                     scale=dcfg.scale, workspace=gws16,
+                                                     stream=stream))
+        g16_bytes = decode_bytes(ginp16)
+        g16_gbs = g16_bytes / (g16_ms * 1e-3) / 1e9
+        out["legs"]["decode_g16"] = {
+            "num_seqs": dcfg.num_seqs, "H": 32, "Hkv": 2, "d": dcfg.d,
+            "total_kv_tokens": int(ginp16.seq_lens.sum()), "bytes": g16_bytes,
+            "ms_mean": round(g16_ms, 4), "GB/s": round(g16_gbs, 1),
+            "frac_of_hbm_peak": round(g16_gbs / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic("decode_g16", "decode_g16")}
+        del gq16, gkc16, gvc16, go16, gws16
 
         # KV append of that chunk size: 8 sequences x 1024 new tokens into a cache
         # with room for 16384 tokens each.
@@ -444,7 +500,8 @@ def main(argv=None):
         out["legs"]["kv_append"] = {
             "num_seqs": B, "n_new": Nq, "Hkv": Hkv, "d": d, "bytes": a_bytes,
             "ms_mean": round(a_ms, 4), "GB/s": round(a_gbs, 1),
-            "frac_of_hbm_peak": round(a_gbs / PEAK_HBM_GBS, 4)}
+            "frac_of_hbm_peak": round(a_gbs / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic("kv_append", "kv_append")}
         del akn, avn, akc, avc
 
     if args.calibrate_copy:

@@ -1,7 +1,6 @@
 // bf16 exact attention (prefill) on gfx950 MFMA, fp32 accumulation: the four-wave kernel
 // behind the two-pass form (fa_fwd_two_pass). Single-pass prefill (fa_fwd, fa_fwd_window,
-// fa_fwd_paged) runs the ping-pong kernel of prefill_pp.hip; its single pass here
-// (PASS = 0) does the same arithmetic in the same order.
+// fa_fwd_paged) runs the ping-pong kernel of prefill_pp.hip.
 //
 // Method (page "Donanıma Duyarlı Algoritma Tasarımı: FlashAttention"):
 // * K and V are split into tiles that are staged in LDS, the CU's fast on-chip
@@ -83,13 +82,13 @@ struct Tile {
 // sweeps K only and keeps each row's running max and sum, leaving the row statistics in
 // HBM as lse = M + ln L; the second recomputes the scores, normalises them directly with
 // those statistics (P = exp(scale s - lse)) and accumulates P V, with no rescaling.
-// PASS = 0 is the usual single pass (not launched by the library).
 template <int D, bool CAUSAL, int PASS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                      float* __restrict__ lse, int H, int Hkv, int Nq, int Nk, int n_qt,
                      int BH, float scale_log2, float tau_raw) {
+    static_assert(PASS == 1 || PASS == 2, "statistics pass, then output pass");
     using T = Tile<D>;
     constexpr int BN = T::BN;
     __shared__ __attribute__((aligned(1024))) char ks0[T::TILE];
@@ -232,13 +231,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             const float m_new = move ? m_cand : m_used;
             const float alpha = move ? fast_exp2((m_used - m_new) * scale_log2) : 1.f;
             m_used = m_new;
-            l_part *= alpha;
-            if constexpr (PASS == 0) {
-#pragma unroll
-                for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-            }
+            l_part *= alpha;  // the first pass keeps no output to rescale
         }
         }
         const float mb = PASS == 2 ? mb_fixed : m_used * scale_log2;
@@ -314,27 +307,24 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         if (j + 1 < n_tiles) step(j + 1, P1{}, std::true_type{});
     }
 
-    // ---- epilogue: O = O_acc / l, lse = M + ln L ----
-    const float l = l_part + xor32(l_part);
-    if (PASS == 1) {  // statistics only
+    // ---- epilogue: the first pass stores lse = M + ln L, the second O (normalised already) ----
+    if constexpr (PASS == 1) {
+        const float l = l_part + xor32(l_part);
         if (qrow < Nq && g == 0)
             lse[(size_t)pair * Nq + qrow] = (m_used * scale_log2 + fast_log2(l)) * kLn2;
         return;
     }
     if (qrow < Nq) {
-        const float inv = PASS == 2 ? 1.f : 1.f / l;  // the second pass is normalised already
         uint16_t* orow = o + ((size_t)pair * Nq + qrow) * D;
 #pragma unroll
         for (int db = 0; db < T::DB; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int d0 = db * 32 + r * 8 + g * 4;
-                u32x2 pk = {pack_bf16x2(oacc[db][r * 4 + 0] * inv, oacc[db][r * 4 + 1] * inv),
-                            pack_bf16x2(oacc[db][r * 4 + 2] * inv, oacc[db][r * 4 + 3] * inv)};
+                u32x2 pk = {pack_bf16x2(oacc[db][r * 4 + 0], oacc[db][r * 4 + 1]),
+                            pack_bf16x2(oacc[db][r * 4 + 2], oacc[db][r * 4 + 3])};
                 *reinterpret_cast<u32x2*>(orow + d0) = pk;
             }
-        if (PASS == 0 && lse != nullptr && g == 0)
-            lse[(size_t)pair * Nq + qrow] = (m_used * scale_log2 + fast_log2(l)) * kLn2;
     }
 }
 

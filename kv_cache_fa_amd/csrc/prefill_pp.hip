@@ -477,9 +477,19 @@ hipError_t launch_pp(const void* q, const void* k, const void* v, void* o, float
 
 }  // namespace
 
+// Work decomposition by launch size: 256-row work-groups that each sweep their rows' whole
+// key range when there are at least as many of them as compute units (256); below that the
+// launch would leave compute units idle and last as long as one work-group's sweep, so the
+// key-split kernel takes it (32-row work-groups, keys shared by four waves).
+constexpr int kComputeUnits = 256;
+
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                            hipStream_t stream) {
+    const long long pp_groups = (long long)((Nq + TilePP<128>::BM - 1) / TilePP<128>::BM) * B * H;
+    if (pp_groups < kComputeUnits)
+        return launch_fwd_bf16_key_split(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale,
+                                         stream);
     if (d == 128)
         return causal
                    ? launch_pp<128, true, false>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, stream)

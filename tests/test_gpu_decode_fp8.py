@@ -97,19 +97,22 @@ def test_fp8_decode_many_sequences():
         assert np.all(inputs.bf16_bits_to_f32(o_h[s]) == 0.0) and np.all(lse_h[s] == -np.inf)
 
 
-def test_fp8_decode_pairs_with_padding_columns():
-    """40 sequences, H8 Hkv4 (g = 2): KV heads read in pairs, two padding columns per head."""
-    base = inputs.custom_decode(40, 8, 4, 128, 1, 900, seed=48)
-    _check(inputs.quantize_decode_fp8(base), "fp8 pairs g=2")
+@pytest.mark.parametrize("S,H,Hkv", [(40, 8, 4), (40, 12, 6), (36, 8, 8), (33, 4, 4)])
+def test_fp8_decode_grouped_kv_heads_with_padding_columns(S, H, Hkv):
+    """KV heads read in pairs with padding columns (32 sequences or more, an even KV head
+    count, g <= 4): H8 Hkv4 and H12 Hkv6 (g = 2: two padding columns per head), H8 Hkv8
+    and H4 Hkv4 (g = 1: three per head)."""
+    base = inputs.custom_decode(S, H, Hkv, 128, 1, 900, seed=48 + Hkv)
+    _check(inputs.quantize_decode_fp8(base), f"fp8 S{S} H{H} Hkv{Hkv}")
 
 
-@pytest.mark.parametrize("S", [8, 40])
-def test_fp8_edge_lengths_and_nan_slots(S):
+@pytest.mark.parametrize("S,H,Hkv", [(8, 8, 2), (40, 8, 2), (40, 16, 4)])
+def test_fp8_edge_lengths_and_nan_slots(S, H, Hkv):
     """Empty sequence, page boundaries; unused slots hold e4m3 NaN bytes and the table is
     padded with -1: the output must equal the zero-filled cache's bit for bit. 8 sequences
-    take the one-KV-head kernel; 40 (H8 Hkv2, g = 4) the kernel that reads two KV heads'
-    rows as one."""
-    cfg = inputs.DecodeConfig("edges", S, 8, 2, 128, 0, 0, 16, 600, 1 / math.sqrt(128), 3)
+    take the one-KV-head kernel; 40 (H8 Hkv2 and H16 Hkv4, g = 4) the kernel that reads two
+    KV heads' rows as one."""
+    cfg = inputs.DecodeConfig("edges", S, H, Hkv, 128, 0, 0, 16, 600, 1 / math.sqrt(128), 3)
     lens = ([0, 1, 15, 16, 17, 64, 65, 600] * (S // 8))[:S]
     a = inputs.quantize_decode_fp8(inputs.make_decode(cfg, seq_lens=lens))
     b = inputs.quantize_decode_fp8(inputs.make_decode(cfg, seq_lens=lens, unused_fill="nan",

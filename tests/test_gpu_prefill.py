@@ -92,9 +92,36 @@ SHAPES = [
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(str(int(x)) for x in s))
 def test_bf16_shapes(shape):
+    """These launches have fewer 256-row blocks than compute units, so fa_fwd runs them on
+    the key-split kernel (32-row work-groups, keys shared by four waves)."""
     B, H, Hkv, Nq, Nk, d, causal = shape
+    assert _pp_groups(B, H, Nq) < 256
     inp = inputs.custom_prefill(B, H, Hkv, Nq, Nk, d, causal, "bf16", seed=sum(shape))
     _dense_check(inp, f"bf16 {shape}")
+
+
+def _pp_groups(B, H, Nq):
+    return -(-Nq // 256) * B * H
+
+
+# The same kinds of edge (ragged tails, GQA/MQA, bottom-right causal, one query, one key
+# tile) with enough (batch, head) pairs that fa_fwd runs the ping-pong kernel.
+SHAPES_PP = [
+    (1, 256, 32, 300, 300, 128, True),
+    (2, 128, 16, 77, 300, 128, True),
+    (1, 256, 256, 130, 129, 64, False),
+    (1, 256, 1, 1, 5, 64, False),
+    (4, 64, 8, 257, 257, 64, True),
+    (2, 128, 128, 1, 1, 128, True),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES_PP, ids=lambda s: "x".join(str(int(x)) for x in s))
+def test_bf16_shapes_ping_pong(shape):
+    B, H, Hkv, Nq, Nk, d, causal = shape
+    assert _pp_groups(B, H, Nq) >= 256
+    inp = inputs.custom_prefill(B, H, Hkv, Nq, Nk, d, causal, "bf16", seed=sum(shape))
+    _dense_check(inp, f"bf16 ping-pong {shape}")
 
 
 @pytest.mark.parametrize("shape", [

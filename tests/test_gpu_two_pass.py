@@ -3,9 +3,11 @@
 Page "Donanıma Duyarlı Algoritma Tasarımı: FlashAttention", section "FlashAttention-1
 (İki Geçişli Yaklaşım)": a statistics pass writes each row's (M, L) (here as lse) and an
 output pass renormalises recomputed scores with them. Checked against the fp64 oracle,
-and against the single-pass kernel: the statistics pass runs the single pass's
-arithmetic without the P.V products, so its lse must match fa_fwd's bit for bit, and the
-two outputs must agree to the bf16 bar.
+and against the single-pass kernel: the statistics pass runs the ping-pong kernel's
+arithmetic without the P.V products, so where fa_fwd runs that kernel (launches with at
+least 256 blocks of 256 rows) its lse must match fa_fwd's bit for bit; where fa_fwd runs
+the key-split kernel the two lse agree up to summation order. The two outputs must agree
+to the bf16 bar.
 """
 import sys
 
@@ -43,6 +45,8 @@ def run_both(inp):
     (1, 4, 1, 300, 450, 128, False),
     (2, 8, 2, 1024, 1024, 64, True),     # d = 64
     (1, 2, 2, 1, 77, 128, True),         # one query
+    (1, 256, 32, 300, 450, 128, True),   # fa_fwd on the ping-pong kernel
+    (2, 128, 128, 77, 77, 64, False),    # the same, d = 64
 ], ids=lambda x: str(x))
 def test_two_pass_vs_oracle_and_single_pass(B, H, Hkv, Nq, Nk, d, causal):
     inp = inputs.custom_prefill(B, H, Hkv, Nq, Nk, d, causal, seed=Nq + Nk + d)
@@ -51,7 +55,10 @@ def test_two_pass_vs_oracle_and_single_pass(B, H, Hkv, Nq, Nk, d, causal):
     q, k, v = inp.as_f64()
     O, L = oracle.attention(q, k, v, causal=causal, scale=inp.cfg.scale)
     check_bf16(inputs.bf16_bits_to_f64(o2), l2, O, L, "two-pass vs oracle")
-    assert np.array_equal(l2, l1), "statistics pass lse differs from the single pass"
+    if -(-Nq // 256) * B * H >= 256:
+        assert np.array_equal(l2, l1), "statistics pass lse differs from the single pass"
+    else:
+        assert np.abs(l2 - l1).max() <= 1e-4, "statistics pass lse vs the key-split kernel's"
     mx, _ = errors(inputs.bf16_bits_to_f64(o2), inputs.bf16_bits_to_f64(o1))
     assert mx <= BF16_MAX_ABS, f"two-pass vs single-pass max-abs {mx}"
 

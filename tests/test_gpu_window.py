@@ -67,9 +67,10 @@ def test_window_zero_selects_own_value_row():
 
 @pytest.mark.parametrize("d", [128, 64])
 def test_window_minus_one_zero_is_the_causal_kernel(d):
-    """(-1, 0) is plain causal: bit-identical to fa_fwd(causal=True)."""
+    """(-1, 0) is plain causal: bit-identical to fa_fwd(causal=True) (256 query heads, so
+    that fa_fwd runs the same ping-pong kernel rather than the key-split one)."""
     import torch
-    inp = inputs.custom_prefill(2, 8, 2, 700, 900, d, True, seed=5 + d)
+    inp = inputs.custom_prefill(2, 128, 16, 700, 900, d, True, seed=5 + d)
     _say(f"[window] (-1,0) vs causal d{d}")
     o_w, l_w = run_window(inp, -1, 0)
     c = inp.cfg
