@@ -70,6 +70,13 @@ __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt field");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// Waits until every LDS read of this wave has returned. A direct load into an LDS stage
+// must not be issued before the reads of the stage's previous tile are done: the hardware
+// does not order a read still in the LDS queue before a later load's write to the same
+// bytes, and the compiler may interleave the load with the reads' MFMAs.
+__device__ __forceinline__ void wait_lds_reads() {
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -253,6 +260,7 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         for (int i = 0; i < n_my; i += 2) {
             const int j = w + T::NW * i;
             tile(j, st0);
+            wait_lds_reads();
             load_v(j + 2 * T::NW, st0);
             const int j1 = j + T::NW;
             if (i + 1 < n_my) {
@@ -260,6 +268,7 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             } else {
                 load_k(j1 + T::NW);
             }
+            wait_lds_reads();
             load_v(j1 + 2 * T::NW, st1);
         }
         wait_vm<0>();  // the loads of the tiles past the end land before the stages are reused

@@ -477,17 +477,21 @@ hipError_t launch_pp(const void* q, const void* k, const void* v, void* o, float
 
 }  // namespace
 
-// Work decomposition by launch size: 256-row work-groups that each sweep their rows' whole
-// key range when there are at least as many of them as compute units (256); below that the
-// launch would leave compute units idle and last as long as one work-group's sweep, so the
-// key-split kernel takes it (32-row work-groups, keys shared by four waves).
+// Work decomposition by launch size. The ping-pong kernel's 256-row work-groups each sweep
+// their rows' whole key range; with few of them the launch lasts as long as one sweep while
+// most compute units idle. The key-split kernel (32-row work-groups, keys shared by four
+// waves) shortens that chain 4x but reads every K/V tile once per 32 rows instead of once
+// per 256, which makes it slower once the chip has work for every compute unit. Measured
+// (MI355X): key-split faster at up to 64 ping-pong work-groups (B2 H8 N1024 d64 causal
+// 20.3 -> 15.0 us, B1 H8 N1024 d128 causal 25.0 -> 13.7 us), mixed at 128 (d64 faster,
+// d128 slower), slower at 256 and beyond.
 constexpr int kComputeUnits = 256;
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                            hipStream_t stream) {
     const long long pp_groups = (long long)((Nq + TilePP<128>::BM - 1) / TilePP<128>::BM) * B * H;
-    if (pp_groups < kComputeUnits)
+    if (pp_groups <= kComputeUnits / 4)
         return launch_fwd_bf16_key_split(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale,
                                          stream);
     if (d == 128)

@@ -112,7 +112,7 @@ def test_paged_prefill_equal_lengths():
 def test_paged_prefill_bit_identical_to_contiguous(d, causal):
     """The paged kernel does the contiguous kernel's arithmetic on the same values: per
     sequence, fa_fwd on its contiguous K/V must give the same bits. (256 query heads, so
-    that fa_fwd's launch fills the chip and runs the same ping-pong kernel.)"""
+    that fa_fwd's launch is large enough to run the same ping-pong kernel.)"""
     torch = _torch()
     ci = inputs.custom_chunked_prefill(4, 256, 32, d, 150, 150, 1300, seed=17 + d)
     _describe(ci, f"bit-identity d{d} causal={causal}")
