@@ -46,9 +46,9 @@ LEG_SOURCES = {
     "prefill_sliding_window": ["prefill_pp.hip", "prefill_common.h"] + _COMMON,
     "prefill_gqa_causal_two_pass": ["prefill_bf16.hip", "prefill_common.h"] + _COMMON,
     "backward_gqa_causal": ["backward.hip", "prefill_common.h"] + _COMMON,
-    "decode": ["decode.hip"] + _COMMON,
-    "decode_fp8": ["decode.hip"] + _COMMON,
-    "decode_g16": ["decode.hip"] + _COMMON,
+    "decode": ["decode.hip", "prefill_common.h"] + _COMMON,
+    "decode_fp8": ["decode.hip", "prefill_common.h"] + _COMMON,
+    "decode_g16": ["decode.hip", "prefill_common.h"] + _COMMON,
     "kv_append": ["kv_append.hip"] + _COMMON,
 }
 

@@ -26,9 +26,16 @@
 //   instruction 1 KiB of whole rows, 16-byte chunks XOR-swizzled by row) into a
 //   per-wave double buffer, and the A operand is read from there without bank
 //   conflicts.
-// * P.V: plain FMAs. A lane owns one 16-byte chunk of V rows (8 dims) for a subset of
-//   the page's tokens and accumulates all heads of the group; the probabilities reach
-//   it through a small per-wave LDS table.
+// * P.V, bf16 cache with one KV head per work-group: O^T[dim][head] += V^T P^T on
+//   v_mfma_f32_16x16x16_bf16. The score accumulator of S^T already holds P^T in the B
+//   operand's layout (lane: head column n, tokens 4 kq .. 4 kq + 3), so the probabilities
+//   never leave the lane; V pages go HBM -> LDS like K (second per-wave double buffer)
+//   and come back as the A operand through transposing reads (ds_read_b64_tr_b16). The
+//   accumulator is 4 fp32 per 16 dims per lane whatever the head count (a 16-head group
+//   held 128 per lane on FMAs, one wave per SIMD).
+// * P.V otherwise (e4m3 cache, KV head pairs): plain FMAs. A lane owns one 16-byte chunk
+//   of V rows (8 dims) for a subset of the page's tokens and accumulates all heads of the
+//   group; the probabilities reach it through a small per-wave LDS table.
 // * A segment's partial result (normalised O_k, lse_k in log2 units) goes to the
 //   caller's workspace, slot k = its work-group's index among those covering the
 //   sequence; a second kernel merges a sequence's slots in order.
@@ -37,6 +44,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "prefill_common.h"
 
 namespace kvfa {
 
@@ -80,7 +88,7 @@ DecodePlan decode_plan(int num_seqs, int max_seq_len) {
 template <bool FP8>
 using ScalePtr = std::conditional_t<FP8, const float*, std::nullptr_t>;
 
-template <int D, int GH, bool FP8, bool PAIR = false>
+template <int D, int GH, bool FP8, bool PAIR = false, bool MMA = false>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kcache,
     const void* __restrict__ vcache, const int32_t* __restrict__ page_table,
@@ -105,18 +113,35 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     constexpr int PAGEB = kPage * ROWB;            // bytes of one page's K rows
     constexpr int KDMA = PAGEB / 1024;             // 1 KiB direct loads per page
     static_assert(KDMA >= 1 && KDMA * 1024 == PAGEB, "whole 1 KiB loads per page");
+    constexpr bool MPV = MMA;                      // P.V on the matrix unit
+    static_assert(!MMA || (!FP8 && !PAIR), "matrix-unit P.V: bf16 cache, one KV head");
+    constexpr int VB = D / 16;                     // 16-dim blocks of O^T (MPV)
     // Per wave: two K stages (separate arrays, so the compiler can tell a read of one from
     // the direct loads into the other); after the wave's loop its partial output for the
     // cross-wave merge reuses the first stage when it fits.
     __shared__ __attribute__((aligned(1024))) char kst_a[kWaves][PAGEB];
     __shared__ __attribute__((aligned(1024))) char kst_b[kWaves][PAGEB];
+    // V stages of the matrix-unit P.V (same shape as the K stages).
+    __shared__ __attribute__((aligned(1024))) char vst_a[kWaves][MPV ? PAGEB : 16];
+    __shared__ __attribute__((aligned(1024))) char vst_b[kWaves][MPV ? PAGEB : 16];
+    // The waves' partial outputs [GH][D] for the cross-wave merge: in the first K stage
+    // when they fit, with MPV in both K stages (rows of heads [0, HPS) in the first),
+    // else in an array of their own.
     constexpr bool RO_IN_A = GH * D * 4 <= PAGEB;
-    __shared__ float red_o_x[RO_IN_A ? 1 : kWaves * GH * D];
-    auto red_o = [&](int ww) -> float* {  // [GH][D] of wave ww
-        if constexpr (RO_IN_A) return reinterpret_cast<float*>(kst_a[ww]);
-        else return red_o_x + ww * GH * D;
+    constexpr bool RO_IN_AB = MPV && !RO_IN_A;
+    static_assert(!RO_IN_AB || GH * D * 4 <= 2 * PAGEB, "two K stages hold the partial output");
+    __shared__ float red_o_x[RO_IN_A || RO_IN_AB ? 1 : kWaves * GH * D];
+    auto red_o_row = [&](int ww, int hh) -> float* {  // head hh's D floats of wave ww
+        if constexpr (RO_IN_A) {
+            return reinterpret_cast<float*>(kst_a[ww]) + hh * D;
+        } else if constexpr (RO_IN_AB) {
+            constexpr int HPS = PAGEB / (D * 4);
+            return reinterpret_cast<float*>(hh < HPS ? kst_a[ww] : kst_b[ww]) + (hh % HPS) * D;
+        } else {
+            return red_o_x + (ww * GH + hh) * D;
+        }
     };
-    __shared__ float p_lds[kWaves][kPage][GH];
+    __shared__ float p_lds[kWaves][MPV ? 1 : kPage][MPV ? 1 : GH];
     __shared__ float a_lds[kWaves][GH];
     __shared__ float red_m[kWaves][GH];
     __shared__ float red_l[kWaves][GH];
@@ -170,8 +195,35 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         const int b = (32 * j + 8 * kq) * ES;
         kr_off[j] = n * ROWB + (((b / 16) ^ (n % KCH)) * 16) + b % 16;
     }
+    // MPV: V stage rows are tokens of ROWB bytes, 16-byte chunks XOR-swizzled by row so that
+    // a transposing read (16-lane group kq: tokens 4 kq + e, e = 0..3, 8 bytes of dims
+    // 16 vb + 4 a each) and its neighbour group (tokens 4 kq + 4 + e), which the LDS serves
+    // together, hit 32 different bank pairs.
+    auto v_swz_dec = [](int r) -> int {
+        if constexpr (ROWB == 256) return 4 * (r & 3) + 2 * ((r >> 2) & 1);
+        else return 2 * ((r >> 1) & 3);
+    };
+    static_assert(!MPV || ROWB == 256 || ROWB == 128, "MPV: d = 128 or 64");
+    uint32_t vd_off[MPV ? KDMA : 1];
+    int vr_off[MPV ? VB : 1];
+    if constexpr (MPV) {
+#pragma unroll
+        for (int i = 0; i < KDMA; ++i) {
+            const int byte = 1024 * i + 16 * lane;
+            const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+            vd_off[i] = (uint32_t)(r * tok_stride * ES + ((pc ^ v_swz_dec(r)) * 16));
+        }
+        // Source lane a + 4 e of group kq points at token 4 kq + e, dims 16 vb + 4 a .. +3:
+        // logical chunk 2 vb + a / 2, byte 8 (a % 2) in it.
+        const int va = lane & 3, vrow = 4 * kq + ((lane >> 2) & 3);
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb)
+            vr_off[vb] = vrow * ROWB + (((2 * vb + (va >> 1)) ^ v_swz_dec(vrow)) * 16) + 8 * (va & 1);
+    }
     char* const kst0 = kst_a[w];
     char* const kst1 = kst_b[w];
+    char* const vst0 = vst_a[w];
+    char* const vst1 = vst_b[w];
     auto load8 = [&](__amdgpu_buffer_rsrc_t r, uint32_t off) -> KVec {
         if constexpr (FP8) return buf_load8_nt(r, off);
         else return buf_load16_nt(r, off);
@@ -195,11 +247,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     // P.V: this lane's chunk c of the row belongs to KV head kc of the NK; it accumulates
     // that head's G2 columns.
     const int kc = PAIR ? c / (D / 8) : 0;
-    float oacc[G2][8];
+    float oacc[MPV ? 1 : G2][8];
 #pragma unroll
-    for (int hh = 0; hh < G2; ++hh)
+    for (int hh = 0; hh < (MPV ? 1 : G2); ++hh)
 #pragma unroll
         for (int e = 0; e < 8; ++e) oacc[hh][e] = 0.f;
+    // MPV: O^T block vb, element i = dim 16 vb + 4 kq + i of head column n.
+    f32x4 macc[MPV ? VB : 1];
+#pragma unroll
+    for (int vb = 0; vb < (MPV ? VB : 1); ++vb) macc[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // This wave's pages are first_page + w + kWaves*i, i < n_my. Lane i holds the
     // physical id of the i-th one, so no page-table load sits on the loop's critical path.
@@ -210,31 +266,48 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     // load, so reading it inside the loop does not wait for the page loads in flight.
     __asm__ volatile("" : "+v"(pid_lane));
 
-    auto load_page = [&](int it, char* kst, KVec (&vv)[TPL]) -> bool {
+    auto load_page = [&](int it, char* kst, KVec (&vv)[TPL], char* vst) -> bool {
         const int pid = __builtin_amdgcn_readlane(pid_lane, it);
         const bool valid = (unsigned)pid < (unsigned)num_pages;
         const size_t page_base = (size_t)(valid ? pid : 0) * kPage * tok_stride + (size_t)kvh * D;
         const auto rk = make_rsrc(static_cast<const char*>(kcache) + page_base * ES, valid ? span : 0u);
-        const auto rv = make_rsrc(static_cast<const char*>(vcache) + page_base * ES, valid ? span : 0u);
+        if constexpr (MPV) {
+            // The stages are rewritten only after this wave's reads of them have returned
+            // (the LDS does not order a queued read before a later direct load's write).
+            __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+        }
 #pragma unroll
         for (int i = 0; i < KDMA; ++i) buf_load16_lds_nt(rk, kst + 1024 * i, kd_off[i], 0u);
+        if constexpr (MPV) {
+            // V rows past the sequence's last token may hold anything; the descriptor ends
+            // at the page's last valid row, so they arrive as zeros (0 x NaN would poison
+            // the product even with a zero probability).
+            const int nv = min(max(t1 - (first_page + w + kWaves * it) * kPage, 0), kPage);
+            const uint32_t vspan = valid && nv > 0 ? (uint32_t)((nv - 1) * tok_stride + DR) * ES : 0u;
+            const auto rv = make_rsrc(static_cast<const char*>(vcache) + page_base * ES, vspan);
 #pragma unroll
-        for (int i = 0; i < TPL; ++i)
-            vv[i] = load8(rv, v_off + (uint32_t)(TG * i * tok_stride) * ES);
+            for (int i = 0; i < KDMA; ++i) buf_load16_lds_nt(rv, vst + 1024 * i, vd_off[i], 0u);
+        } else {
+            const auto rv = make_rsrc(static_cast<const char*>(vcache) + page_base * ES, valid ? span : 0u);
+#pragma unroll
+            for (int i = 0; i < TPL; ++i)
+                vv[i] = load8(rv, v_off + (uint32_t)(TG * i * tok_stride) * ES);
+        }
         return valid;
     };
 
     KVec vA[TPL], vB[TPL];
-    bool okA = load_page(0, kst0, vA);   // a lane past the wave's pages holds id -1
+    bool okA = load_page(0, kst0, vA, vst0);   // a lane past the wave's pages holds id -1
     bool okB = false;
     // Every load of the page before this one's successor has landed: its K rows in LDS
-    // (direct loads are counted by vmcnt only) and its V registers.
+    // (direct loads are counted by vmcnt only) and its V registers (MPV: V rows in LDS).
     auto wait_page = [&]() __attribute__((always_inline)) {
-        constexpr int later = KDMA + TPL;  // loads of the page issued after it
+        constexpr int later = KDMA + (MPV ? KDMA : TPL);  // loads of the page issued after it
         static_assert(later < 64, "vmcnt field");
         __builtin_amdgcn_s_waitcnt((later & 15) | ((later >> 4) << 14) | (7 << 4) | (15 << 8));
     };
-    auto page_compute = [&](const char* KST, const KVec (&VV)[TPL], const bool OK, const int IT) {
+    auto page_compute = [&](const char* KST, const KVec (&VV)[TPL], const char* VST, const bool OK,
+                            const int IT) {
         if (OK) {
             const int tok0 = (first_page + w + kWaves * IT) * kPage;
             KVec KF[KS];
@@ -262,14 +335,39 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
             const float m_cand = fmaxf(m_used, mx);  // finite: a page's first token is valid
             const bool move = m_cand > m_used + tau_raw;
             const bool resc = __builtin_amdgcn_ballot_w64(move) != 0;
+            float alpha = 1.f;  // alpha = 1 for unmoved heads
             if (resc) {
-                const float m_new = move ? m_cand : m_used;  // alpha = 1 for unmoved heads
-                const float alpha = move ? fast_exp2((m_used - m_new) * scale_log2) : 1.f;
+                const float m_new = move ? m_cand : m_used;
+                alpha = move ? fast_exp2((m_used - m_new) * scale_log2) : 1.f;
                 m_used = m_new;
                 l_part *= alpha;
-                if (kq == 0 && n < GH) a_lds[w][n] = alpha;
+                if constexpr (!MPV)
+                    if (kq == 0 && n < GH) a_lds[w][n] = alpha;
             }
             const float mb = m_used * scale_log2;
+            if constexpr (MPV) {
+                // P^T as the B operand: this lane's column n, tokens 4 kq .. 4 kq + 3 (bf16;
+                // the row sum takes the unrounded values).
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] = fast_exp2(fmaf(acc[i], scale_log2, -mb));
+                    l_part += p[i];
+                }
+                const u32x2 pf = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+                if (resc) {
+#pragma unroll
+                    for (int vb = 0; vb < VB; ++vb) macc[vb] *= alpha;  // column n is this lane's
+                }
+#pragma unroll
+                for (int vb = 0; vb < VB; ++vb) {
+                    const u32x2 a = prefill::lds_read_tr(VST + vr_off[vb]);
+                    macc[vb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                        __builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, pf), macc[vb],
+                        0, 0, 0);
+                }
+                return;
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float p = fast_exp2(fmaf(acc[i], scale_log2, -mb));
@@ -313,12 +411,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         }
     };
     for (int it = 0; it < n_my; it += 2) {
-        okB = load_page(it + 1, kst1, vB);
+        okB = load_page(it + 1, kst1, vB, vst1);
         wait_page();
-        page_compute(kst0, vA, okA, it);
-        okA = load_page(it + 2, kst0, vA);
+        page_compute(kst0, vA, vst0, okA, it);
+        okA = load_page(it + 2, kst0, vA, vst0);
         wait_page();
-        page_compute(kst1, vB, okB, it + 1);
+        page_compute(kst1, vB, vst1, okB, it + 1);
     }
     // The loop ends with two pages' loads still in flight (past the wave's last page: zero
     // descriptors, but their LDS writes land in the stages reused below).
@@ -328,25 +426,37 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     float l = l_part;
     l += shfl_xor(l, 16);
     l += shfl_xor(l, 32);
-#pragma unroll
-    for (int hh = 0; hh < G2; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = oacc[hh][e];
-#pragma unroll
-            for (int msk = CH; msk < 64; msk <<= 1) x += shfl_xor(x, msk);
-            oacc[hh][e] = x;
-        }
     if (kq == 0 && n < GH) {
         red_m[w][n] = m_used;
         red_l[w][n] = l;
     }
-    if (tg == 0) {
-        float* ro = red_o(w);
+    if constexpr (MPV) {
+        // The matrix unit summed over the tokens already: lane (n, kq) holds dims
+        // 16 vb + 4 kq + i of head column n.
+        if (n < nheads) {
+            float* ro = red_o_row(w, n);
+#pragma unroll
+            for (int vb = 0; vb < VB; ++vb)
+                *reinterpret_cast<f32x4*>(ro + 16 * vb + 4 * kq) = macc[vb];
+        }
+    } else {
 #pragma unroll
         for (int hh = 0; hh < G2; ++hh)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ro[(kc * G2 + hh) * D + (c % (D / 8)) * 8 + e] = oacc[hh][e];
+            for (int e = 0; e < 8; ++e) {
+                float x = oacc[hh][e];
+#pragma unroll
+                for (int msk = CH; msk < 64; msk <<= 1) x += shfl_xor(x, msk);
+                oacc[hh][e] = x;
+            }
+        if (tg == 0) {
+#pragma unroll
+            for (int hh = 0; hh < G2; ++hh) {
+                float* ro = red_o_row(w, kc * G2 + hh) + (c % (D / 8)) * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ro[e] = oacc[hh][e];
+            }
+        }
     }
     __syncthreads();
 
@@ -371,7 +481,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
                 const float mw = red_m[ww][hh];  // -inf for a wave that saw no token
                 const float f = mw == -INFINITY ? 0.f : fast_exp2((mw - M) * sc);
                 lsum = fmaf(f, red_l[ww][hh], lsum);
-                acc = fmaf(f, red_o(ww)[hh * D + dd], acc);
+                acc = fmaf(f, red_o_row(ww, hh)[dd], acc);
             }
         }
         const size_t row = ((size_t)s * H + head) * max_slots + slot;
@@ -613,11 +723,12 @@ DecodeWorkspace decode_workspace(void* ws, int num_seqs, int H, int d, int max_s
 
 // Work-groups aimed at: one round of resident ones (two for an fp8 cache, whose ranges take
 // half the time) shared by the (KV head, head group) pairs: 256 CUs (MI355X) times the
-// work-groups a CU holds by the kernels' register use, 3 for 4 heads per group, 2 for 8,
-// 1 for 16. (Fixed numbers: no runtime query precedes the launch.)
+// work-groups a CU holds. FMA P.V: by register use, 3 for 4 heads per group, 2 for 8, 1 for
+// 16. Matrix-unit P.V: by LDS (four K/V page stages per wave), 2 for d = 128 (66 KiB
+// each), 4 for d = 64. (Fixed numbers: no runtime query precedes the launch.)
 constexpr int kCUs = 256;
-int decode_target(int GH, bool fp8, int groups) {
-    const int per_cu = GH == 4 ? 3 : GH == 8 ? 2 : 1;
+int decode_target(int GH, bool mma, int groups, int d, bool fp8) {
+    const int per_cu = mma ? (d == 128 ? 2 : 4) : GH == 4 ? 3 : GH == 8 ? 2 : 1;
     return std::max(1, per_cu * kCUs * (fp8 ? 2 : 1) / groups);
 }
 // Pairs: one round of the pair kernel's work-groups per CU (3 for bf16 with d = 64, else 2,
@@ -632,7 +743,7 @@ int decode_max_rows(const DecodePlan& plan, int num_seqs) {
     return std::max(std::max(3 * kCUs * 2, plan.min_wgs), num_seqs);
 }
 
-template <int D, int GH, bool FP8, bool PAIR = false>
+template <int D, int GH, bool FP8, bool PAIR = false, bool MMA = false>
 hipError_t launch_split(const void* q, const void* kc, const void* vc, const int32_t* pt,
                         const int32_t* sl, const DecodeWorkspace& ws, const DecodePlan& plan,
                         int target, int rows, int num_seqs, int H, int Hkv, int g, int n_hg,
@@ -643,7 +754,7 @@ hipError_t launch_split(const void* q, const void* kc, const void* vc, const int
     // together, so each physical page (all KV heads of 16 slots, contiguous) is read by
     // concurrently running work-groups.
     dim3 grid(Hkv * n_hg / (PAIR ? 2 : 1), rows);
-    hipLaunchKernelGGL((decode_split_kernel<D, GH, FP8, PAIR>), grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((decode_split_kernel<D, GH, FP8, PAIR, MMA>), grid, dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), kc, vc, pt, sl, ws.o_part, ws.lse_part,
                        ws.n_slots, num_seqs > 64 ? ws.plan : nullptr, num_seqs, H, Hkv, g, n_hg,
                        num_pages, max_pages, max_seq_len,
@@ -652,7 +763,7 @@ hipError_t launch_split(const void* q, const void* kc, const void* vc, const int
 }
 
 template <int D, bool FP8>
-hipError_t launch_split_d(int GH, bool pair, const void* q, const void* kc, const void* vc,
+hipError_t launch_split_d(int GH, bool pair, bool mma, const void* q, const void* kc, const void* vc,
                           const int32_t* pt, const int32_t* sl, const DecodeWorkspace& ws,
                           const DecodePlan& plan, int target, int rows, int num_seqs, int H,
                           int Hkv, int g, int n_hg, int num_pages, int max_pages,
@@ -663,6 +774,20 @@ hipError_t launch_split_d(int GH, bool pair, const void* q, const void* kc, cons
             return launch_split<D, 8, FP8, true>(q, kc, vc, pt, sl, ws, plan, target, rows,
                                                   num_seqs, H, Hkv, g, n_hg, num_pages,
                                                   max_pages, max_seq_len, scale, ks, vs, stream);
+    if constexpr (!FP8)
+        if (mma) {
+            if (GH == 4)
+                return launch_split<D, 4, false, false, true>(
+                    q, kc, vc, pt, sl, ws, plan, target, rows, num_seqs, H, Hkv, g, n_hg,
+                    num_pages, max_pages, max_seq_len, scale, ks, vs, stream);
+            if (GH == 8)
+                return launch_split<D, 8, false, false, true>(
+                    q, kc, vc, pt, sl, ws, plan, target, rows, num_seqs, H, Hkv, g, n_hg,
+                    num_pages, max_pages, max_seq_len, scale, ks, vs, stream);
+            return launch_split<D, 16, false, false, true>(
+                q, kc, vc, pt, sl, ws, plan, target, rows, num_seqs, H, Hkv, g, n_hg, num_pages,
+                max_pages, max_seq_len, scale, ks, vs, stream);
+        }
     if (GH == 4)
         return launch_split<D, 4, FP8>(q, kc, vc, pt, sl, ws, plan, target, rows, num_seqs, H, Hkv, g, n_hg,
                                        num_pages, max_pages, max_seq_len, scale, ks, vs, stream);
@@ -712,7 +837,14 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
     // pairs would halve them (1 x 8192 tokens, H32 Hkv8 d128: 15.3 us single, 16.6 paired).
     const bool pair = (d * (fp8 ? 1 : 2) == 128 || (!fp8 && d == 128)) && Hkv % 2 == 0 &&
                       g <= 4 && num_seqs >= 32;
-    const int target = pair ? decode_target_pair(Hkv / 2, fp8, d) : decode_target(GH, fp8, Hkv * n_hg);
+    // Single KV heads of a bf16 cache: P.V on the matrix unit, except for groups of up to 4
+    // heads over 32 or more sequences, where the FMA kernel's third resident work-group per
+    // CU (the matrix-unit kernel's V stages leave room for two) reads faster (64 x U{512..8192},
+    // H28 Hkv7: 177.6 us on FMAs, 200.4 us on the matrix unit; 16 x 1024, H32 Hkv8: 22.7 vs
+    // 16.9 us; 64 x U{512..8192}, H32 Hkv2: 93.2 vs 65.2 us).
+    const bool mma = !fp8 && !pair && (GH >= 8 || num_seqs < 32);
+    const int target = pair ? decode_target_pair(Hkv / 2, fp8, d)
+                            : decode_target(GH, mma, Hkv * n_hg, d, fp8);
     const int rows = std::max(std::max(target, plan.min_wgs), num_seqs);  // <= decode_max_rows
 
     hipError_t e;
@@ -723,20 +855,20 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
         if (e != hipSuccess) return e;
     }
     if (d == 128)
-        e = fp8 ? launch_split_d<128, true>(GH, pair, q, k_cache, v_cache, page_table, seq_lens, ws,
+        e = fp8 ? launch_split_d<128, true>(GH, pair, mma, q, k_cache, v_cache, page_table, seq_lens, ws,
                                             plan, target, rows, num_seqs, H, Hkv, g, n_hg, num_pages,
                                             max_pages_per_seq, max_seq_len, scale, k_scale,
                                             v_scale, stream)
-                : launch_split_d<128, false>(GH, pair, q, k_cache, v_cache, page_table, seq_lens, ws,
+                : launch_split_d<128, false>(GH, pair, mma, q, k_cache, v_cache, page_table, seq_lens, ws,
                                              plan, target, rows, num_seqs, H, Hkv, g, n_hg, num_pages,
                                              max_pages_per_seq, max_seq_len, scale, nullptr,
                                              nullptr, stream);
     else
-        e = fp8 ? launch_split_d<64, true>(GH, pair, q, k_cache, v_cache, page_table, seq_lens, ws,
+        e = fp8 ? launch_split_d<64, true>(GH, pair, mma, q, k_cache, v_cache, page_table, seq_lens, ws,
                                            plan, target, rows, num_seqs, H, Hkv, g, n_hg, num_pages,
                                            max_pages_per_seq, max_seq_len, scale, k_scale,
                                            v_scale, stream)
-                : launch_split_d<64, false>(GH, pair, q, k_cache, v_cache, page_table, seq_lens, ws,
+                : launch_split_d<64, false>(GH, pair, mma, q, k_cache, v_cache, page_table, seq_lens, ws,
                                             plan, target, rows, num_seqs, H, Hkv, g, n_hg, num_pages,
                                             max_pages_per_seq, max_seq_len, scale, nullptr,
                                             nullptr, stream);

@@ -87,6 +87,8 @@ def test_decode_edge_lengths():
     (1500, 4, 1, 64, 40, 64, 45),         # the planning kernel's 1024-length passes, twice
     (48, 8, 8, 128, 600, 1024, 46),       # KV head pairs with g = 1 (3 padding columns each)
     (40, 16, 8, 64, 500, 1024, 47),       # pairs, g = 2, d = 64
+    (100, 32, 2, 128, 600, 1024, 48),     # g = 16, P.V on the matrix unit, planned ranges
+    (70, 16, 2, 64, 900, 1024, 49),       # g = 8, d = 64, matrix-unit P.V
 ], ids=lambda x: str(x))
 def test_decode_many_sequences(S, H, Hkv, d, hi, max_seq_len, seed):
     """More than 64 sequences (the in-kernel page count and prefix sums run over chunks of
@@ -101,11 +103,14 @@ def test_decode_many_sequences(S, H, Hkv, d, hi, max_seq_len, seed):
         assert np.all(inputs.bf16_bits_to_f32(o_h[s]) == 0.0) and np.all(lse_h[s] == -np.inf)
 
 
-@pytest.mark.parametrize("S", [12, 40])  # 40: KV heads read in pairs
-def test_unused_slots_and_table_padding_are_never_read(S):
+@pytest.mark.parametrize("S,H,Hkv", [(12, 16, 4), (40, 16, 4), (40, 32, 2), (50, 12, 3)])
+def test_unused_slots_and_table_padding_are_never_read(S, H, Hkv):
     """Slots past a sequence's length hold NaN and unused table entries hold -1: the
-    output must be bit-identical to the zero-filled cache's."""
-    cfg = inputs.DecodeConfig("nan", S, 16, 4, 128, 1, 900, 16, 1024, 1 / math.sqrt(128), 11)
+    output must be bit-identical to the zero-filled cache's. 12 sequences: one KV head per
+    work-group, P.V on the matrix unit (V rows past the sequence must arrive as zeros, since
+    0 x NaN is NaN); 40 with H16 Hkv4: KV heads read in pairs (FMA P.V); 40 with H32 Hkv2:
+    16 heads per KV head on the matrix unit; 50 with H12 Hkv3: one KV head, FMA P.V."""
+    cfg = inputs.DecodeConfig("nan", S, H, Hkv, 128, 1, 900, 16, 1024, 1 / math.sqrt(128), 11)
     a = inputs.make_decode(cfg)
     b = inputs.make_decode(cfg, unused_fill="nan", table_pad=-1)
     assert np.array_equal(a.seq_lens, b.seq_lens)
@@ -117,12 +122,12 @@ def test_unused_slots_and_table_padding_are_never_read(S):
     check_bf16(inputs.bf16_bits_to_f64(ob), lb, O, L, "nan-filled cache")
 
 
-@pytest.mark.parametrize("S", [16, 40])  # 40: KV heads read in pairs
-def test_peaked_query_selects_cached_value_bit_exactly(S):
+@pytest.mark.parametrize("S,H,Hkv", [(16, 32, 8), (40, 32, 8), (40, 32, 4)])
+def test_peaked_query_selects_cached_value_bit_exactly(S, H, Hkv):
     """q[s,h] = 64 * K_s[t*] for a seeded target token t* per (sequence, head): every
     other exponential underflows to exactly 0, so O[s,h] must equal the stored
     V_s[t*] bit for bit. A wrong page, slot or head index cannot pass."""
-    cfg = inputs.DecodeConfig("peak", S, 32, 8, 128, 1, 3000, 16, 3000, 1 / math.sqrt(128), 17)
+    cfg = inputs.DecodeConfig("peak", S, H, Hkv, 128, 1, 3000, 16, 3000, 1 / math.sqrt(128), 17)
     inp = inputs.make_decode(cfg)
     rng = np.random.default_rng(99)
     g = cfg.H // cfg.Hkv
