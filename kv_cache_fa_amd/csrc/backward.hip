@@ -77,6 +77,12 @@ __device__ __forceinline__ void buf_load4_lds(__amdgpu_buffer_rsrc_t r, void* ld
 #ifndef DKDV_WAVES
 #define DKDV_WAVES 2
 #endif
+#ifndef BWD_AHEAD
+#define BWD_AHEAD 2
+#endif
+#ifndef DQ_AHEAD
+#define DQ_AHEAD 2
+#endif
 
 template <int D>
 struct BwdTile {
@@ -96,25 +102,31 @@ struct BwdTile {
 // the A operand of a 32x32x16 MFMA read as rows (row = 32 kb + col, chunk 2s + g), and
 // the same tile read transposed (ds_read_b64_tr_b16; rows 16t + 4(G/2) + e and those
 // plus 8, chunk 4db + 2(G%2) + a/2, byte 8(a%2), G = lane/16, lane%16 = a + 4e).
+// The logical chunk is a constant part (2s, 4db: high bits) OR'ed with a per-lane part
+// (low bits), so its XOR with the swizzle is the constant part XOR (per-lane part ^
+// swizzle): each offset is two instructions from two per-lane values, instead of one
+// register per k-step held across the loop.
 template <int D>
 struct TileReads {
-    int row_off[D / 16];   // + kb * 32 * ROW
-    int tr_off0[D / 32];   // rows 16t + vrow      (+ t * 16 * ROW)
-    int tr_off1[D / 32];   // rows 16t + vrow + 8  (+ t * 16 * ROW)
+    int row_base, row_x;            // col * ROW, g ^ kt_swz(col)
+    int tr_base0, tr_x0;            // rows 16t + vrow
+    int tr_base1, tr_x1;            // rows 16t + vrow + 8
     __device__ __forceinline__ void init(int lane) {
         constexpr int ROW = D * 2;
         const int col = lane & 31, g = lane >> 5;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) row_off[s] = col * ROW + (((2 * s + g) ^ kt_swz<D>(col)) * 16);
+        row_base = col * ROW;
+        row_x = g ^ kt_swz<D>(col);
         const int vG = lane >> 4, va = lane & 3, ve = (lane >> 2) & 3;
         const int vrow = (vG >> 1) * 4 + ve;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            const int lc = 4 * db + 2 * (vG & 1) + (va >> 1);
-            tr_off0[db] = vrow * ROW + ((lc ^ kt_swz<D>(vrow)) * 16) + 8 * (va & 1);
-            tr_off1[db] = (vrow + 8) * ROW + ((lc ^ kt_swz<D>(vrow + 8)) * 16) + 8 * (va & 1);
-        }
+        const int lcb = 2 * (vG & 1) + (va >> 1);
+        tr_base0 = vrow * ROW + 8 * (va & 1);
+        tr_x0 = lcb ^ kt_swz<D>(vrow);
+        tr_base1 = (vrow + 8) * ROW + 8 * (va & 1);
+        tr_x1 = lcb ^ kt_swz<D>(vrow + 8);
     }
+    __device__ __forceinline__ int row_off(int s) const { return row_base + (((2 * s) ^ row_x) << 4); }
+    __device__ __forceinline__ int tr_off0(int db) const { return tr_base0 + (((4 * db) ^ tr_x0) << 4); }
+    __device__ __forceinline__ int tr_off1(int db) const { return tr_base1 + (((4 * db) ^ tr_x1) << 4); }
 };
 
 // Direct-load offsets: piece i of wave w covers tile bytes [1024 (NP w + i), +1024); lane L
@@ -128,6 +140,23 @@ __device__ __forceinline__ void dma_offsets(int w, int lane, uint32_t (&off)[NP]
         const int r = byte / ROW, pc = (byte % ROW) / 16;
         off[i] = (uint32_t)(r * ROW + ((pc ^ kt_swz<D>(r)) * 16));
     }
+}
+
+// Schedules for a block of N MFMAs whose A operands are LDS reads (R reads per MFMA): the
+// reads run AHEAD MFMAs ahead of their use, so the LDS latency overlaps the matrix work
+// instead of stalling every MFMA.
+// ID keeps each block's pattern apart from the others' (and from the other LDS reads).
+// A block is N steps of M MFMAs fed by R reads; the reads run AHEAD steps ahead.
+template <int N, int R, int AHEAD, int ID, int M = 1>
+__device__ __forceinline__ void sched_reads_ahead() {
+    static_assert(N > AHEAD, "block longer than the read-ahead");
+    __builtin_amdgcn_sched_group_barrier(0x100, R * AHEAD, ID);  // DS reads
+#pragma unroll
+    for (int i = 0; i < N - AHEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, M, ID);      // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, R, ID);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, M * AHEAD, ID);
 }
 
 // A 16-key (or 16-query) step of a transposed product: reads the 4 + 4 rows of the
@@ -153,6 +182,11 @@ void dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     __shared__ __attribute__((aligned(1024))) char ds1[T::QT];
     __shared__ __attribute__((aligned(256))) float st0[2][64];  // lse, D of the tile's rows
     __shared__ __attribute__((aligned(256))) float st1[2][64];
+    // d = 128: each wave's 32 K rows stay in LDS (kt_swz-swizzled like the Q tiles) instead
+    // of 32 registers per lane, which buys the registers that let the LDS operand reads run
+    // ahead of the MFMAs (two work-groups per CU still fit: 65 KiB each).
+    constexpr bool KLDS = D == 128;
+    __shared__ __attribute__((aligned(1024))) char krow[KLDS ? 4 : 1][KLDS ? T::QT : 1024];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -171,11 +205,19 @@ void dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // The wave's K and V rows as B operands: K[key][16s + 8g .. +7].
     const auto rk = make_rsrc(k + (size_t)bk * Nk * D, (uint32_t)Nk * D * 2);
     const auto rv = make_rsrc(v + (size_t)bk * Nk * D, (uint32_t)Nk * D * 2);
-    u32x4 kf[T::KS], vf[T::KS];
+    u32x4 kf[KLDS ? 1 : T::KS], vf[T::KS];
 #pragma unroll
     for (int s = 0; s < T::KS; ++s) {
-        kf[s] = buf_load16(rk, (uint32_t)(key * D + 16 * s + 8 * g) * 2);
+        if constexpr (!KLDS) kf[s] = buf_load16(rk, (uint32_t)(key * D + 16 * s + 8 * g) * 2);
         vf[s] = buf_load16(rv, (uint32_t)(key * D + 16 * s + 8 * g) * 2);
+    }
+    char* const kw = krow[KLDS ? w : 0];
+    if constexpr (KLDS) {  // rows k0 + 32 w .. +31 into this wave's region (read after a barrier)
+        uint32_t koff[T::QT / 1024];
+        dma_offsets<D, T::QT / 1024>(0, lane, koff);
+#pragma unroll
+        for (int i = 0; i < T::QT / 1024; ++i)
+            buf_load16_lds(rk, kw + 1024 * i, koff[i], (uint32_t)(k0 + 32 * w) * (uint32_t)T::ROW);
     }
 
     // Query tiles: causal rows before k0 - off never see this block's keys.
@@ -189,9 +231,16 @@ void dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     TileReads<D> rd;
     rd.init(lane);
 
-    auto load_tile = [&](int t, char* qdst, char* ddst, float (*sdst)[64]) {
-        const int h = kvh * gq + t / per_head;
-        const int qt = qt0 + t % per_head;
+    // Tiles go head by head, query tile by query tile: (head offset hq, query tile qt),
+    // advanced by a counter instead of a division per tile.
+    auto advance = [&](int& hq, int& qt) {
+        if (++qt == n_qt) {
+            qt = qt0;
+            ++hq;
+        }
+    };
+    auto load_tile = [&](int hq, int qt, char* qdst, char* ddst, float (*sdst)[64]) {
+        const int h = kvh * gq + hq;
         const size_t pair = (size_t)b * H + h;
         const auto rq = make_rsrc(q + pair * Nq * D, (uint32_t)Nq * D * 2);
         const auto rdo = make_rsrc(dout + pair * Nq * D, (uint32_t)Nq * D * 2);
@@ -215,16 +264,21 @@ void dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         dva[i] = f32x16{};
     }
 
-    auto tile = [&](int t, const char* qst, const char* dst, const float (*sst)[64]) {
-        const int qt = qt0 + t % per_head;
+    auto tile = [&](int qt, const char* qst, const char* dst, const float (*sst)[64]) {
         const int q0 = qt * T::BQ;
         // S[q][key]: lane holds rows q = 8(i/4) + 4g + i%4 of its key column.
         f32x16 sa = f32x16{};
 #pragma unroll
         for (int s = 0; s < T::KS; ++s) {
-            const u32x4 aq = *reinterpret_cast<const u32x4*>(qst + rd.row_off[s]);
-            sa = mfma32x32x16(aq, kf[s], sa);
+            const u32x4 aq = *reinterpret_cast<const u32x4*>(qst + rd.row_off(s));
+            if constexpr (KLDS) {
+                const u32x4 bk = *reinterpret_cast<const u32x4*>(kw + rd.row_off(s));
+                sa = mfma32x32x16(aq, bk, sa);
+            } else {
+                sa = mfma32x32x16(aq, kf[s], sa);
+            }
         }
+        sched_reads_ahead<T::KS, KLDS ? 2 : 1, BWD_AHEAD, 1>();
         // P = exp(scale s - lse), zero outside the mask and past Nq; packed for the
         // 16-query steps (rows 16t' + 4g + {0..3}, then 16t' + 8 + 4g + {0..3}).
         u32x4 pp[2];
@@ -233,15 +287,26 @@ void dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             const int rl = 8 * r + 4 * g;
             const f32x4 lv = *reinterpret_cast<const f32x4*>(&sst[0][rl]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int qa = q0 + rl + e;
-                bool ok = qa < Nq;
-                if (CAUSAL) ok = ok && key <= qa + off;
-                // computed unconditionally and then selected: a conditional exponential
-                // becomes a branch per element
-                const float ex = fast_exp2(fmaf(sa[4 * r + e], scale_log2, -lv[e] * kLog2e));
-                sa[4 * r + e] = ok ? ex : 0.f;
-            }
+            for (int e = 0; e < 4; ++e)
+                sa[4 * r + e] = fast_exp2(fmaf(sa[4 * r + e], scale_log2, -lv[e] * kLog2e));
+        }
+        // Only tiles that reach past Nq or cross the causal diagonal of the block's keys
+        // need the mask (a uniform branch; the exponentials above are computed either way,
+        // then selected: a conditional exponential becomes a branch per element).
+        const bool whole = q0 + T::BQ <= Nq && (!CAUSAL || q0 + off >= k0 + 127);
+        if (!whole) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int qa = q0 + 8 * r + 4 * g + e;
+                    bool ok = qa < Nq;
+                    if (CAUSAL) ok = ok && key <= qa + off;
+                    sa[4 * r + e] = ok ? sa[4 * r + e] : 0.f;
+                }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
             const int tt = r >> 1, half = (r & 1) * 2;
             pp[tt][half] = pack_bf16x2(sa[4 * r], sa[4 * r + 1]);
             pp[tt][half + 1] = pack_bf16x2(sa[4 * r + 2], sa[4 * r + 3]);
@@ -251,16 +316,18 @@ void dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int db = 0; db < T::DB; ++db) {
-                const u32x4 ado = tr_operand(dst + tt * 16 * T::ROW, rd.tr_off0[db], rd.tr_off1[db]);
+                const u32x4 ado = tr_operand(dst + tt * 16 * T::ROW, rd.tr_off0(db), rd.tr_off1(db));
                 dva[db] = mfma32x32x16(ado, pp[tt], dva[db]);
             }
+        sched_reads_ahead<2 * T::DB, 2, BWD_AHEAD, 2>();
         // dP[q][key] = dO V^T, then dS = P (dP - D), packed like P.
         f32x16 pa = f32x16{};
 #pragma unroll
         for (int s = 0; s < T::KS; ++s) {
-            const u32x4 ad = *reinterpret_cast<const u32x4*>(dst + rd.row_off[s]);
+            const u32x4 ad = *reinterpret_cast<const u32x4*>(dst + rd.row_off(s));
             pa = mfma32x32x16(ad, vf[s], pa);
         }
+        sched_reads_ahead<T::KS, 1, BWD_AHEAD, 3>();
         u32x4 ps[2];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -278,21 +345,33 @@ void dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int db = 0; db < T::DB; ++db) {
-                const u32x4 aq = tr_operand(qst + tt * 16 * T::ROW, rd.tr_off0[db], rd.tr_off1[db]);
+                const u32x4 aq = tr_operand(qst + tt * 16 * T::ROW, rd.tr_off0(db), rd.tr_off1(db));
                 dka[db] = mfma32x32x16(aq, ps[tt], dka[db]);
             }
+        sched_reads_ahead<2 * T::DB, 2, BWD_AHEAD, 4>();
     };
 
     if (n_tiles > 0) {
-        load_tile(0, qs0, ds0, st0);
+        int ld_hq = 0, ld_qt = qt0;  // next tile to load
+        int cp_hq = 0, cp_qt = qt0;  // next tile to compute
+        load_tile(ld_hq, ld_qt, qs0, ds0, st0);
+        advance(ld_hq, ld_qt);
         __syncthreads();
         for (int t = 0; t < n_tiles; t += 2) {
-            if (t + 1 < n_tiles) load_tile(t + 1, qs1, ds1, st1);
-            tile(t, qs0, ds0, st0);
+            if (t + 1 < n_tiles) {
+                load_tile(ld_hq, ld_qt, qs1, ds1, st1);
+                advance(ld_hq, ld_qt);
+            }
+            tile(cp_qt, qs0, ds0, st0);
+            advance(cp_hq, cp_qt);
             __syncthreads();
             if (t + 1 < n_tiles) {
-                if (t + 2 < n_tiles) load_tile(t + 2, qs0, ds0, st0);
-                tile(t + 1, qs1, ds1, st1);
+                if (t + 2 < n_tiles) {
+                    load_tile(ld_hq, ld_qt, qs0, ds0, st0);
+                    advance(ld_hq, ld_qt);
+                }
+                tile(cp_qt, qs1, ds1, st1);
+                advance(cp_hq, cp_qt);
                 __syncthreads();
             }
         }
@@ -395,12 +474,13 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             pa[kb] = f32x16{};
 #pragma unroll
             for (int s = 0; s < T::KS; ++s) {
-                const u32x4 ak = *reinterpret_cast<const u32x4*>(kst + rd.row_off[s] + kb * 32 * T::ROW);
-                const u32x4 av = *reinterpret_cast<const u32x4*>(vst + rd.row_off[s] + kb * 32 * T::ROW);
+                const u32x4 ak = *reinterpret_cast<const u32x4*>(kst + rd.row_off(s) + kb * 32 * T::ROW);
+                const u32x4 av = *reinterpret_cast<const u32x4*>(vst + rd.row_off(s) + kb * 32 * T::ROW);
                 sa[kb] = mfma32x32x16(ak, qf[s], sa[kb]);
                 pa[kb] = mfma32x32x16(av, dof[s], pa[kb]);
             }
         }
+        sched_reads_ahead<KB * T::KS, 2, DQ_AHEAD, 5, 2>();
         // dS^T for key rows 32kb + 8(i/4) + 4g + i%4 of this lane's query, packed for the
         // 16-key steps (rows 16t + 4g + {0..3}, then 16t + 8 + 4g + {0..3}).
         const int lim = CAUSAL ? min(Nk - 1, qrow + off) - j * BN - 4 * g : Nk - 1 - j * BN - 4 * g;
@@ -425,7 +505,7 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             }
 #pragma unroll
             for (int db = 0; db < T::DB; ++db) {
-                const u32x4 a = tr_operand(kst + t * 16 * T::ROW, rd.tr_off0[db], rd.tr_off1[db]);
+                const u32x4 a = tr_operand(kst + t * 16 * T::ROW, rd.tr_off0(db), rd.tr_off1(db));
                 dqa[db] = mfma32x32x16(a, ps, dqa[db]);
             }
         }
