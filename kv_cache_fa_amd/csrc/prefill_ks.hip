@@ -109,6 +109,10 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const auto rq = make_rsrc(q + (size_t)pair * Nq * D, (uint32_t)Nq * D * 2);
     const auto rk = make_rsrc(k + ((size_t)b * Hkv + kvh) * Nk * D, (uint32_t)Nk * D * 2);
     const auto rv = make_rsrc(v + ((size_t)b * Hkv + kvh) * Nk * D, (uint32_t)Nk * D * 2);
+    // Zero-size descriptors for the loads of tiles past the row block's last one: they still
+    // count as issued loads (the waits keep fixed counts) but fetch nothing.
+    const auto rk_none = make_rsrc(k, 0u);
+    const auto rv_none = make_rsrc(v, 0u);
 
     // Key tiles of the row block, and the first one that needs a mask.
     const int n_all = (Nk + BN - 1) / BN;
@@ -132,13 +136,14 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     u32x4 kf[T::KB][T::KS];
     const uint32_t k_lane = (uint32_t)(col * D * 2 + g * 16);
     auto load_k = [&](int j) {
+        const auto r = j < n_tiles ? rk : rk_none;
         const uint32_t tile_off = (uint32_t)j * (uint32_t)T::TILE;
 #pragma unroll
         for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
             for (int s = 0; s < T::KS; ++s)
                 kf[kb][s] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rk, k_lane + (uint32_t)(kb * 32 * D * 2 + s * 32), tile_off, 0);
+                    r, k_lane + (uint32_t)(kb * 32 * D * 2 + s * 32), tile_off, 0);
     };
     // V tile j into one stage: the i-th 1 KiB piece covers tile bytes [1024 i, +1024);
     // lane L fills byte 16 L of it, i.e. row r, physical chunk pc, with logical chunk
@@ -151,9 +156,10 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         dv_off[i] = (uint32_t)(r * T::ROW + ((pc ^ v_swz<D>(r)) * 16));
     }
     auto load_v = [&](int j, char* dst) {
+        const auto r = j < n_tiles ? rv : rv_none;
 #pragma unroll
         for (int i = 0; i < T::DMA; ++i)
-            buf_load16_lds(rv, dst + 1024 * i, dv_off[i], (uint32_t)j * (uint32_t)T::TILE);
+            buf_load16_lds(r, dst + 1024 * i, dv_off[i], (uint32_t)j * (uint32_t)T::TILE);
     };
     // V^T operand (t, db, half): rows 16 t + 8 half + 4 (G/2) + e, logical chunk
     // 4 db + 2 (G%2) + a/2, byte 8 (a%2) in it (G = lane/16, lane%16 = a + 4 e).
@@ -174,9 +180,9 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     // One tile: scores, mask (tiles from `full` on), running max, exponentials, P.V. Its V
     // is in stage vst. One body serves masked and unmasked tiles (a copy of each made the
     // compiler keep two register assignments live and spill).
-    // The loads of the tiles after it are issued whether or not those tiles exist (loads
-    // past the end of K/V return zeros; tiles past the row block's last key are only
-    // loaded, never used), so every wait below has one fixed count.
+    // The loads of the tiles after it are issued whether or not those tiles exist (through
+    // zero-size descriptors when they do not: nothing is fetched), so every wait below has
+    // one fixed count.
     auto tile = [&](const int j, const char* vst) {
         f32x16 sacc[T::KB];
 #pragma unroll
