@@ -17,8 +17,8 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                            hipStream_t stream);
 
-// The key-split prefill kernel (32-row work-groups whose four waves share the keys);
-// launch_fwd_bf16 picks it for launches that would not fill the chip otherwise.
+// The key-split prefill kernel (64-row work-groups whose key range runs in four parts);
+// launch_fwd_bf16 picks it for launches of at most 128 blocks of 256 rows.
 hipError_t launch_fwd_bf16_key_split(const void* q, const void* k, const void* v, void* o,
                                      float* lse, int B, int H, int Hkv, int Nq, int Nk, int d,
                                      int causal, float scale, hipStream_t stream);

@@ -1,5 +1,6 @@
-// bf16 exact attention (prefill) for launches too small to fill the chip: each work-group
-// owns 32 query rows of one (batch, head), and its four waves split that tile's keys.
+// bf16 exact attention (prefill) for launches too small to fill the chip with 256-row
+// work-groups: each work-group owns 64 query rows of one (batch, head), and its key range
+// is split into four parts that run side by side.
 //
 // Method (page "Donanıma Duyarlı Algoritma Tasarımı: FlashAttention"): the same tiling and
 // online softmax as the other prefill kernels ("FlashAttention'ın Temelleri", "Online
@@ -12,27 +13,27 @@
 // İyileştirmeler", item 4: the block size is picked per hardware and sequence length;
 // item 1: one head's work is spread over more compute units). The 256-row work-groups of
 // the ping-pong kernel each sweep their row block's whole key range, so when there are
-// fewer of them than compute units the launch lasts as long as the longest sweep, not as
-// long as the chip needs for the work (B2 H8 N1024 d64 causal: 64 work-groups, each up
-// to 16 tiles of 64 keys one after the other). Here the longest chain is a quarter of
-// that and there are 8x as many work-groups.
+// few of them the launch lasts as long as the longest sweep while most compute units idle
+// (B2 H8 N1024 d64 causal: 64 work-groups, each up to 16 tiles of 64 keys one after the
+// other). Here the longest chain is a quarter of that, with 4x as many work-groups.
 //
 // gfx950 mapping:
-// * 256 threads = 4 waves; wave w takes key tiles w, w + 4, w + 8, ... of its row block.
-//   The waves never wait for each other until the merge.
-// * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with the wave's 32 Q rows held as B
-//   operands; each lane owns one query column, so the row max is in-lane plus one
-//   exchange with lane ^ 32. K operands are loaded from memory straight into registers
-//   in the MFMA's layout (a lane reads 16 contiguous bytes of one key row), one tile
-//   ahead of use.
-// * O^T += V^T P^T: V tiles go from memory straight into LDS (buffer_load ... lds), two
-//   stages per wave, two tiles ahead, and are read back through transposing LDS reads
-//   (ds_read_b64_tr_b16), 16-byte chunks XOR-swizzled by row so those reads are
-//   conflict-free.
-// * Merge: every wave writes its (m, l) per row and its fp32 output accumulator to LDS
-//   over its own V stages; after a work-group barrier wave w combines rows' dims
-//   32 db + 8 w + {0..7} of all four parts and stores them as bf16, and wave 0 stores
-//   lse = m + ln l.
+// * 512 threads = 8 waves: row group rg (32 rows) x key part p; part p takes key tiles
+//   p, p + 4, p + 8, ... (64 keys for d = 64, 32 for d = 128). The two waves of a part
+//   (one per row group) share its K and V tiles: each loads half of them straight into
+//   LDS (buffer_load ... lds), double-buffered; a work-group barrier per step publishes
+//   the next tiles. Sharing halves the K/V reads of a four-wave, 32-row design (whose
+//   waves each loaded their own tiles): B2 H8 N1024 d64 causal 14.8 -> 10.2 us.
+// * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K rows from LDS as A (16-byte chunks
+//   XOR-swizzled by row), the wave's 32 Q rows held as B; each lane owns one query
+//   column, so the row max is in-lane plus one exchange with lane ^ 32.
+// * O^T += V^T P^T: V^T through transposing LDS reads (ds_read_b64_tr_b16), swizzled so
+//   they are conflict-free; P^T straight from the score registers.
+// * Loads of tiles past the work-group's last one go through zero-size descriptors
+//   (nothing is fetched), so every step issues the same loads.
+// * Merge: every wave writes its (m, l) per row and its fp32 accumulator to LDS over the
+//   K/V stages; after a barrier wave (rg, p) combines dims 32 db + 8 p + {0..7} of its
+//   row group's four parts and stores them as bf16, and part 0 stores lse = m + ln l.
 #include <type_traits>
 
 #include "common.h"
@@ -46,57 +47,48 @@ using namespace prefill;
 
 template <int D>
 struct TileKS {
-    static constexpr int NW = 4;                 // waves per work-group (key parts)
+    static constexpr int RG = 2;                 // row groups (32 rows each)
+    static constexpr int KP = 4;                 // key parts
+    static constexpr int NW = RG * KP;           // waves per work-group
     static constexpr int NT = 64 * NW;           // threads per work-group
-    static constexpr int BM = 32;                // query rows per work-group
+    static constexpr int BM = 32 * RG;           // query rows per work-group
     static constexpr int BN = D == 64 ? 64 : 32; // keys per tile
     static constexpr int KB = BN / 32;           // 32-key blocks of S^T
     static constexpr int KS = D / 16;            // MFMA k-steps of Q.K (16 dims each)
     static constexpr int DB = D / 32;            // 32-dim blocks of O^T
     static constexpr int PS = BN / 16;           // MFMA k-steps of P.V (16 keys each)
     static constexpr int ROW = D * 2;            // bytes per K/V row
-    static constexpr int TILE = BN * ROW;        // bytes of one V tile
-    static constexpr int DMA = TILE / 1024;      // 1 KiB direct loads per V tile (one wave)
-    static constexpr int KL = KB * KS;           // 16-byte K loads per lane per tile
+    static constexpr int TILE = BN * ROW;        // bytes of one K (or V) tile
+    static constexpr int HALF = TILE / 1024 / RG;  // 1 KiB direct loads per wave per tile
     static constexpr int PART = DB * 16 * 64 * 4;  // bytes of one wave's fp32 accumulator
-    static_assert(DMA * 1024 == TILE && PART <= 2 * TILE, "merge area fits in the V stages");
-    static_assert(PART % 1024 == 0, "whole 1 KiB chunks");
-    static_assert(2 * KL + DMA < 64, "vmcnt field");
+    static_assert(HALF >= 1 && HALF * 1024 * RG == TILE, "whole 1 KiB loads per wave");
+    static_assert(PART <= 2 * TILE, "merge area fits in a part's stages");
 };
 
-// Waits until at most n vector-memory loads of this wave are in flight (n constant).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// Waits until every LDS read of this wave has returned. A direct load into an LDS stage
-// must not be issued before the reads of the stage's previous tile are done: the hardware
-// does not order a read still in the LDS queue before a later load's write to the same
-// bytes, and the compiler may interleave the load with the reads' MFMAs.
-__device__ __forceinline__ void wait_lds_reads() {
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
-}
-
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                    float* __restrict__ lse, int H, int Hkv, int Nq, int Nk, int n_qt, int BH,
                    float scale_log2, float tau_raw) {
     using T = TileKS<D>;
     constexpr int BN = T::BN;
-    // V stages of wave w: vs0[w], vs1[w] (separate arrays, so the compiler can tell a load
-    // into one stage from reads of the other); reused for the merge.
-    __shared__ __attribute__((aligned(1024))) char vs0[T::NW][T::TILE];
-    __shared__ __attribute__((aligned(1024))) char vs1[T::NW][T::TILE];
+    // Stage s of key part p: K in ks<s>[p], V in vs<s>[p] (separate arrays, so the compiler
+    // can tell a load into one stage from reads of the other); reused for the merge.
+    // 128 KiB: one work-group per CU, two waves per SIMD.
+    __shared__ __attribute__((aligned(1024))) char ks0[T::KP][T::TILE];
+    __shared__ __attribute__((aligned(1024))) char ks1[T::KP][T::TILE];
+    __shared__ __attribute__((aligned(1024))) char vs0[T::KP][T::TILE];
+    __shared__ __attribute__((aligned(1024))) char vs1[T::KP][T::TILE];
     __shared__ float red[T::NW][2][32];  // per wave: m (log2 units) and l of each row
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int col = lane & 31;  // query row (column of S^T) owned by this lane
-    const int g = lane >> 5;    // which half of the MFMA k-slots this lane supplies
+    const int kp = w & (T::KP - 1);   // key part
+    const int rg = w / T::KP;         // row group
+    const int col = lane & 31;        // query row (column of S^T) owned by this lane
+    const int g = lane >> 5;          // which half of the MFMA k-slots this lane supplies
 
     int pair, qt;
     map_work(blockIdx.x, n_qt, BH, H / Hkv, CAUSAL, pair, qt);
@@ -104,26 +96,24 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const int kvh = h / (H / Hkv);
     const int q0 = qt * T::BM;
     const int off = Nk - Nq;
-    const int qrow = q0 + col;
+    const int qrow = q0 + 32 * rg + col;
 
     const auto rq = make_rsrc(q + (size_t)pair * Nq * D, (uint32_t)Nq * D * 2);
     const auto rk = make_rsrc(k + ((size_t)b * Hkv + kvh) * Nk * D, (uint32_t)Nk * D * 2);
     const auto rv = make_rsrc(v + ((size_t)b * Hkv + kvh) * Nk * D, (uint32_t)Nk * D * 2);
-    // Zero-size descriptors for the loads of tiles past the row block's last one: they still
-    // count as issued loads (the waits keep fixed counts) but fetch nothing.
+    // Zero-size descriptors for the loads of tiles past the last one: nothing is fetched.
     const auto rk_none = make_rsrc(k, 0u);
     const auto rv_none = make_rsrc(v, 0u);
 
-    // Key tiles of the row block, and the first one that needs a mask.
+    // Key tiles of the work-group's rows, and this wave's first tile that needs a mask.
     const int n_all = (Nk + BN - 1) / BN;
     int n_tiles = n_all, full = Nk / BN;
     if (CAUSAL) {
         const int last_row = min(q0 + T::BM, Nq) - 1;
         n_tiles = min(n_all, (last_row + off) / BN + 1);
-        full = min(full, (q0 + off + 1) / BN);
+        full = min(full, (q0 + 32 * rg + off + 1) / BN);
     }
-    // This wave's tiles: j_i = w + 4 i, i < n_my.
-    const int n_my = w < n_tiles ? (n_tiles - w + T::NW - 1) / T::NW : 0;
+    const int steps = (n_tiles + T::KP - 1) / T::KP;  // part p takes tiles p, p + 4, ...
 
     // B operand of S^T = K Q^T: Q[qrow][16 s + 8 g .. +7]; rows past Nq load as zero.
     u32x4 qf[T::KS];
@@ -131,36 +121,32 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     for (int s = 0; s < T::KS; ++s)
         qf[s] = buf_load16(rq, (uint32_t)(qrow * D + s * 16 + g * 8) * 2);
 
-    // K operand (kb, s) of tile j: K[j BN + 32 kb + col][16 s + 8 g .. +7]; the tile's
-    // offset is uniform (a scalar register), the rest a per-lane base plus a constant.
-    u32x4 kf[T::KB][T::KS];
-    const uint32_t k_lane = (uint32_t)(col * D * 2 + g * 16);
-    auto load_k = [&](int j) {
-        const auto r = j < n_tiles ? rk : rk_none;
-        const uint32_t tile_off = (uint32_t)j * (uint32_t)T::TILE;
+    // Direct loads: this wave fills pieces [HALF rg, HALF rg + HALF) of its part's K and V
+    // tiles; lane L of piece i writes tile byte 1024 i + 16 L: row r, physical chunk pc,
+    // with logical chunk pc ^ swizzle(r) of row r.
+    uint32_t dk_off[T::HALF], dv_off[T::HALF];
 #pragma unroll
-        for (int kb = 0; kb < T::KB; ++kb)
-#pragma unroll
-            for (int s = 0; s < T::KS; ++s)
-                kf[kb][s] = __builtin_amdgcn_raw_buffer_load_b128(
-                    r, k_lane + (uint32_t)(kb * 32 * D * 2 + s * 32), tile_off, 0);
-    };
-    // V tile j into one stage: the i-th 1 KiB piece covers tile bytes [1024 i, +1024);
-    // lane L fills byte 16 L of it, i.e. row r, physical chunk pc, with logical chunk
-    // pc ^ v_swz(r) of row r.
-    uint32_t dv_off[T::DMA];
-#pragma unroll
-    for (int i = 0; i < T::DMA; ++i) {
-        const int byte = 1024 * i + 16 * lane;
+    for (int i = 0; i < T::HALF; ++i) {
+        const int byte = 1024 * (T::HALF * rg + i) + 16 * lane;
         const int r = byte / T::ROW, pc = (byte % T::ROW) / 16;
+        dk_off[i] = (uint32_t)(r * T::ROW + ((pc ^ k_swz<D>(r)) * 16));
         dv_off[i] = (uint32_t)(r * T::ROW + ((pc ^ v_swz<D>(r)) * 16));
     }
-    auto load_v = [&](int j, char* dst) {
-        const auto r = j < n_tiles ? rv : rv_none;
+    auto load = [&](int j, char* kdst, char* vdst) {
+        const bool have = j < n_tiles;
+        const auto r1 = have ? rk : rk_none;
+        const auto r2 = have ? rv : rv_none;
+        const uint32_t toff = (uint32_t)j * (uint32_t)T::TILE;
 #pragma unroll
-        for (int i = 0; i < T::DMA; ++i)
-            buf_load16_lds(r, dst + 1024 * i, dv_off[i], (uint32_t)j * (uint32_t)T::TILE);
+        for (int i = 0; i < T::HALF; ++i) {
+            buf_load16_lds(r1, kdst + 1024 * (T::HALF * rg + i), dk_off[i], toff);
+            buf_load16_lds(r2, vdst + 1024 * (T::HALF * rg + i), dv_off[i], toff);
+        }
     };
+    // K operand (kb, s): row 32 kb + col, logical chunk 2 s + g.
+    int kr_off[T::KS];
+#pragma unroll
+    for (int s = 0; s < T::KS; ++s) kr_off[s] = col * T::ROW + (((2 * s + g) ^ k_swz<D>(col)) * 16);
     // V^T operand (t, db, half): rows 16 t + 8 half + 4 (G/2) + e, logical chunk
     // 4 db + 2 (G%2) + a/2, byte 8 (a%2) in it (G = lane/16, lane%16 = a + 4 e).
     const int vG = lane >> 4, va = lane & 3, ve = (lane >> 2) & 3;
@@ -177,22 +163,18 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < T::DB; ++i) oacc[i] = f32x16{};
 
-    // One tile: scores, mask (tiles from `full` on), running max, exponentials, P.V. Its V
-    // is in stage vst. One body serves masked and unmasked tiles (a copy of each made the
-    // compiler keep two register assignments live and spill).
-    // The loads of the tiles after it are issued whether or not those tiles exist (through
-    // zero-size descriptors when they do not: nothing is fetched), so every wait below has
-    // one fixed count.
-    auto tile = [&](const int j, const char* vst) {
+    // One tile: scores, mask (tiles from `full` on), running max, exponentials, P.V.
+    auto tile = [&](const int j, const char* kst, const char* vst) {
         f32x16 sacc[T::KB];
 #pragma unroll
         for (int kb = 0; kb < T::KB; ++kb) {
             sacc[kb] = f32x16{};
 #pragma unroll
-            for (int s = 0; s < T::KS; ++s)
-                sacc[kb] = mfma32x32x16(kf[kb][s], qf[s], sacc[kb]);
+            for (int s = 0; s < T::KS; ++s) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(kst + kr_off[s] + kb * 32 * T::ROW);
+                sacc[kb] = mfma32x32x16(a, qf[s], sacc[kb]);
+            }
         }
-        load_k(j + T::NW);  // the registers are free once the MFMAs have read them
         if (j >= full) {
             // key offset inside the tile of element (kb, i) is kb*32 + 8*(i/4) + 4g + i%4;
             // it is dead past the row's last key and past Nk.
@@ -228,9 +210,6 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         // causal limit) keeps a -inf reference; its exponentials are taken against 0,
         // which makes them exp2(-inf) = 0.
         const float mb = m_used == -INFINITY ? 0.f : m_used * scale_log2;
-        // V_j has landed once at most the loads issued after it are in flight: K_j, V_{j+4}
-        // and K_{j+4}.
-        wait_vm<2 * T::KL + T::DMA>();
 #pragma unroll
         for (int t = 0; t < T::PS; ++t) {
             const int kb = t >> 1, base = (t & 1) * 8;
@@ -244,7 +223,6 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             }
 #pragma unroll
             for (int db = 0; db < T::DB; ++db) {
-                // keys 16t + 4g + {0..3} and 16t + 8 + 4g + {0..3} at dim 32db + col
                 const u32x2 a0 = lds_read_tr(vst + vr_off[db] + (t * 16) * T::ROW);
                 const u32x2 a1 = lds_read_tr(vst + vr_off[db] + (t * 16 + 8) * T::ROW);
                 const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
@@ -253,40 +231,31 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         }
     };
 
-    // Issue order V_0, K_0, V_1, then per tile i: K_{i+1} after its scores, V_{i+2} after
-    // its P.V, so V_i always has K_i, V_{i+1}, K_{i+1} behind it. Tiles go in pairs (one
-    // per stage); with an odd count the pair's second tile does not exist and only its
-    // K load is issued, so that the loads stay in the same order on both paths.
-    char* st0 = vs0[w];
-    char* st1 = vs1[w];
-    if (n_my > 0) {
-        load_v(w, st0);
-        load_k(w);
-        load_v(w + T::NW, st1);
-        for (int i = 0; i < n_my; i += 2) {
-            const int j = w + T::NW * i;
-            tile(j, st0);
-            wait_lds_reads();
-            load_v(j + 2 * T::NW, st0);
-            const int j1 = j + T::NW;
-            if (i + 1 < n_my) {
-                tile(j1, st1);
-            } else {
-                load_k(j1 + T::NW);
-            }
-            wait_lds_reads();
-            load_v(j1 + 2 * T::NW, st1);
+    // Step i: part p's tile p + 4 i from stage i & 1, while step i + 1's tiles load into the
+    // other stage; the barrier that ends a step completes those loads (both row groups'
+    // halves) and frees the stage just read.
+    load(kp, ks0[kp], vs0[kp]);
+    __syncthreads();
+    for (int i = 0; i < steps; i += 2) {
+        const int j = kp + T::KP * i;
+        load(j + T::KP, ks1[kp], vs1[kp]);
+        if (j < n_tiles) tile(j, ks0[kp], vs0[kp]);
+        __syncthreads();
+        if (i + 1 < steps) {
+            const int j1 = j + T::KP;
+            load(j1 + T::KP, ks0[kp], vs0[kp]);
+            if (j1 < n_tiles) tile(j1, ks1[kp], vs1[kp]);
+            __syncthreads();
         }
-        wait_vm<0>();  // the loads of the tiles past the end land before the stages are reused
     }
 
-    // ---- merge the four parts ----
-    // Every load of this wave has landed, so its V stages are free. Accumulator elements
-    // (db, 4 r .. 4 r + 3) of all 64 lanes form the 1 KiB chunk c = 4 db + r of wave x's
-    // merge area: chunk c of vs0[x], then of vs1[x].
-    constexpr int CPS = T::TILE / 1024;  // chunks per stage
-    auto chunk = [&](int x, int c) -> char* {
-        return c < CPS ? vs0[x] + 1024 * c : vs1[x] + 1024 * (c - CPS);
+    // ---- merge the four parts of each row group ----
+    // All loads are done (the last barrier waited for them). Wave (rg, p)'s accumulator,
+    // 1 KiB chunk c = 4 db + r: chunk c of [ks0|ks1][p] (row group 0|1), then of [vs0|vs1][p].
+    constexpr int CPT = T::TILE / 1024;
+    auto chunk = [&](int rgx, int px, int c) -> char* {
+        char* a = c < CPT ? (rgx == 0 ? ks0[px] : ks1[px]) : (rgx == 0 ? vs0[px] : vs1[px]);
+        return a + 1024 * (c % CPT);
     };
     const float l = l_part + xor32(l_part);
     if (g == 0) {
@@ -297,33 +266,33 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     for (int db = 0; db < T::DB; ++db)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            *reinterpret_cast<f32x4*>(chunk(w, 4 * db + r) + 16 * lane) =
+            *reinterpret_cast<f32x4*>(chunk(rg, kp, 4 * db + r) + 16 * lane) =
                 f32x4{oacc[db][4 * r], oacc[db][4 * r + 1], oacc[db][4 * r + 2], oacc[db][4 * r + 3]};
     __syncthreads();
 
-    // Every row attends key 0, which is in wave 0's first tile, so M is finite.
-    float mw[T::NW], M = -INFINITY;
+    // Every row attends key 0, which is in part 0's first tile, so M is finite.
+    float mw[T::KP], M = -INFINITY;
 #pragma unroll
-    for (int x = 0; x < T::NW; ++x) {
-        mw[x] = red[x][0][col];
+    for (int x = 0; x < T::KP; ++x) {
+        mw[x] = red[rg * T::KP + x][0][col];
         M = fmaxf(M, mw[x]);
     }
-    float a[T::NW], L = 0.f;
+    float a[T::KP], L = 0.f;
 #pragma unroll
-    for (int x = 0; x < T::NW; ++x) {
+    for (int x = 0; x < T::KP; ++x) {
         a[x] = fast_exp2(mw[x] - M);  // 0 for a part that saw no key of the row
-        L += a[x] * red[x][1][col];
+        L += a[x] * red[rg * T::KP + x][1][col];
     }
     const float inv = 1.f / L;
     if (qrow < Nq) {
         uint16_t* orow = o + ((size_t)pair * Nq + qrow) * D;
-        const int r = w;  // this wave stores dims 32 db + 8 w + 4 g .. +3
+        const int r = kp;  // this wave stores dims 32 db + 8 kp + 4 g .. +3 of its rows
 #pragma unroll
         for (int db = 0; db < T::DB; ++db) {
             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int x = 0; x < T::NW; ++x) {
-                const f32x4 p = *reinterpret_cast<const f32x4*>(chunk(x, 4 * db + r) + 16 * lane);
+            for (int x = 0; x < T::KP; ++x) {
+                const f32x4 p = *reinterpret_cast<const f32x4*>(chunk(rg, x, 4 * db + r) + 16 * lane);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) acc[c] = fmaf(a[x], p[c], acc[c]);
             }
@@ -331,7 +300,7 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                               pack_bf16x2(acc[2] * inv, acc[3] * inv)};
             *reinterpret_cast<u32x2*>(orow + db * 32 + r * 8 + g * 4) = pk;
         }
-        if (lse != nullptr && w == 0 && g == 0)
+        if (lse != nullptr && kp == 0 && g == 0)
             lse[(size_t)pair * Nq + qrow] = (M + fast_log2(L)) * kLn2;
     }
 }

@@ -479,19 +479,22 @@ hipError_t launch_pp(const void* q, const void* k, const void* v, void* o, float
 
 // Work decomposition by launch size. The ping-pong kernel's 256-row work-groups each sweep
 // their rows' whole key range; with few of them the launch lasts as long as one sweep while
-// most compute units idle. The key-split kernel (32-row work-groups, keys shared by four
-// waves) shortens that chain 4x but reads every K/V tile once per 32 rows instead of once
-// per 256, which makes it slower once the chip has work for every compute unit. Measured
-// (MI355X): key-split faster at up to 64 ping-pong work-groups (B2 H8 N1024 d64 causal
-// 20.3 -> 15.0 us, B1 H8 N1024 d128 causal 25.0 -> 13.7 us), mixed at 128 (d64 faster,
-// d128 slower), slower at 256 and beyond.
+// most compute units idle. The key-split kernel (64-row work-groups whose key range runs in
+// four parts side by side) shortens that chain 4x but reads every K/V tile once per 64 rows
+// instead of once per 256. Measured (MI355X, us, ping-pong -> key-split): at 64 ping-pong
+// work-groups B2 H8 N1024 d64 causal 20.2 -> 10.2, B1 H8 N2048 d128 causal 43.3 -> 23.8; at
+// 128 B1 H8 N4096 d128 causal 82.2 -> 51.4, B1 H32 Hkv8 N1024 d128 25.9 -> 23.1, but B4 H8
+// N1024 d128 25.8 -> 27.1; at 256 B2 H16 N2048 d64 37.5 -> 39.1. The key-split kernel takes
+// launches of up to 128 ping-pong work-groups (half the compute units) whose key range is
+// longer than two 64-key tiles; with at most 128 keys there is no chain to split, and its
+// barrier and larger work-groups cost ~1 us (B2 H8 N128 d64 causal: 5.9 -> 6.3 us).
 constexpr int kComputeUnits = 256;
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                            hipStream_t stream) {
     const long long pp_groups = (long long)((Nq + TilePP<128>::BM - 1) / TilePP<128>::BM) * B * H;
-    if (pp_groups <= kComputeUnits / 4)
+    if (pp_groups <= kComputeUnits / 2 && Nk > 128)
         return launch_fwd_bf16_key_split(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale,
                                          stream);
     if (d == 128)

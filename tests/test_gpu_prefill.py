@@ -87,16 +87,18 @@ SHAPES = [
     (1, 16, 2, 64, 4100, 128, True),    # long cache, short query block
     (3, 2, 1, 129, 129, 64, False),
     (1, 2, 2, 4097, 4097, 128, True),
+    (2, 4, 2, 1, 777, 64, True),        # one query row over a long cache (key-split kernel)
+    (1, 4, 4, 3, 300, 128, False),      # three rows: one 64-row block, mostly empty
 ]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(str(int(x)) for x in s))
 def test_bf16_shapes(shape):
-    """These launches have at most 64 blocks of 256 rows (a quarter of the compute units),
-    so fa_fwd runs them on the key-split kernel (32-row work-groups, keys shared by four
-    waves)."""
+    """Launches with at most 128 blocks of 256 rows (half the compute units) and more than
+    128 keys run on the key-split kernel (64-row work-groups whose keys run in four parts);
+    the ones with at most 128 keys on the ping-pong kernel."""
     B, H, Hkv, Nq, Nk, d, causal = shape
-    assert _pp_groups(B, H, Nq) <= 64
+    assert _pp_groups(B, H, Nq) <= 128
     inp = inputs.custom_prefill(B, H, Hkv, Nq, Nk, d, causal, "bf16", seed=sum(shape))
     _dense_check(inp, f"bf16 {shape}")
 
@@ -120,7 +122,7 @@ SHAPES_PP = [
 @pytest.mark.parametrize("shape", SHAPES_PP, ids=lambda s: "x".join(str(int(x)) for x in s))
 def test_bf16_shapes_ping_pong(shape):
     B, H, Hkv, Nq, Nk, d, causal = shape
-    assert _pp_groups(B, H, Nq) > 64
+    assert _pp_groups(B, H, Nq) > 128
     inp = inputs.custom_prefill(B, H, Hkv, Nq, Nk, d, causal, "bf16", seed=sum(shape))
     _dense_check(inp, f"bf16 ping-pong {shape}")
 

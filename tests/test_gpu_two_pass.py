@@ -5,7 +5,7 @@ Page "Donanıma Duyarlı Algoritma Tasarımı: FlashAttention", section "FlashAt
 output pass renormalises recomputed scores with them. Checked against the fp64 oracle,
 and against the single-pass kernel: the statistics pass runs the ping-pong kernel's
 arithmetic without the P.V products, so where fa_fwd runs that kernel (launches with more
-than 64 blocks of 256 rows) its lse must match fa_fwd's bit for bit; where fa_fwd runs
+than 128 blocks of 256 rows) its lse must match fa_fwd's bit for bit; where fa_fwd runs
 the key-split kernel the two lse agree up to summation order. The two outputs must agree
 to the bf16 bar.
 """
@@ -55,7 +55,7 @@ def test_two_pass_vs_oracle_and_single_pass(B, H, Hkv, Nq, Nk, d, causal):
     q, k, v = inp.as_f64()
     O, L = oracle.attention(q, k, v, causal=causal, scale=inp.cfg.scale)
     check_bf16(inputs.bf16_bits_to_f64(o2), l2, O, L, "two-pass vs oracle")
-    if -(-Nq // 256) * B * H > 64:
+    if -(-Nq // 256) * B * H > 128:
         assert np.array_equal(l2, l1), "statistics pass lse differs from the single pass"
     else:
         assert np.abs(l2 - l1).max() <= 1e-4, "statistics pass lse vs the key-split kernel's"
