@@ -25,8 +25,10 @@
 //   the next tiles. Sharing halves the K/V reads of a four-wave, 32-row design (whose
 //   waves each loaded their own tiles): B2 H8 N1024 d64 causal 14.8 -> 10.2 us.
 // * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K rows from LDS as A (16-byte chunks
-//   XOR-swizzled by row), the wave's 32 Q rows held as B; each lane owns one query
-//   column, so the row max is in-lane plus one exchange with lane ^ 32.
+//   XOR-swizzled by row), the wave's 32 Q rows held as B (each row group's Q tile is
+//   loaded once into LDS for its four parts and read from there: 10.3 -> 9.8 us on B2 H8
+//   N1024 d64 causal); each lane owns one query column, so the row max is in-lane plus
+//   one exchange with lane ^ 32.
 // * O^T += V^T P^T: V^T through transposing LDS reads (ds_read_b64_tr_b16), swizzled so
 //   they are conflict-free; P^T straight from the score registers.
 // * Loads of tiles past the work-group's last one go through zero-size descriptors
@@ -75,12 +77,15 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     constexpr int BN = T::BN;
     // Stage s of key part p: K in ks<s>[p], V in vs<s>[p] (separate arrays, so the compiler
     // can tell a load into one stage from reads of the other); reused for the merge.
-    // 128 KiB: one work-group per CU, two waves per SIMD.
+    // 128 KiB (+ the Q tiles): one work-group per CU, two waves per SIMD.
     __shared__ __attribute__((aligned(1024))) char ks0[T::KP][T::TILE];
     __shared__ __attribute__((aligned(1024))) char ks1[T::KP][T::TILE];
     __shared__ __attribute__((aligned(1024))) char vs0[T::KP][T::TILE];
     __shared__ __attribute__((aligned(1024))) char vs1[T::KP][T::TILE];
     __shared__ float red[T::NW][2][32];  // per wave: m (log2 units) and l of each row
+    // Each row group's 32 Q rows, loaded once for its four parts (16-byte chunks swizzled
+    // by row like the K tiles, so the 32 rows read together hit different banks).
+    __shared__ __attribute__((aligned(1024))) char qs[T::RG][32 * T::ROW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -116,10 +121,18 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const int steps = (n_tiles + T::KP - 1) / T::KP;  // part p takes tiles p, p + 4, ...
 
     // B operand of S^T = K Q^T: Q[qrow][16 s + 8 g .. +7]; rows past Nq load as zero.
-    u32x4 qf[T::KS];
+    // The row group's tile arrives by direct loads (part p fills 1 KiB pieces p, p + 4, ...)
+    // before the first barrier, and each wave reads its operands from it after that.
+    constexpr int QP = 32 * T::ROW / 1024;  // 1 KiB pieces of a row group's Q tile
+    static_assert(QP % T::KP == 0, "whole pieces per part");
 #pragma unroll
-    for (int s = 0; s < T::KS; ++s)
-        qf[s] = buf_load16(rq, (uint32_t)(qrow * D + s * 16 + g * 8) * 2);
+    for (int i = kp; i < QP; i += T::KP) {
+        const int byte = 1024 * i + 16 * lane;
+        const int r = byte / T::ROW, pc = (byte % T::ROW) / 16;
+        buf_load16_lds(rq, qs[rg] + 1024 * i, (uint32_t)(r * T::ROW + ((pc ^ k_swz<D>(r)) * 16)),
+                       (uint32_t)(q0 + 32 * rg) * (uint32_t)T::ROW);
+    }
+    u32x4 qf[T::KS];
 
     // Direct loads: this wave fills pieces [HALF rg, HALF rg + HALF) of its part's K and V
     // tiles; lane L of piece i writes tile byte 1024 i + 16 L: row r, physical chunk pc,
@@ -236,6 +249,10 @@ void fwd_ks_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     // halves) and frees the stage just read.
     load(kp, ks0[kp], vs0[kp]);
     __syncthreads();
+#pragma unroll
+    for (int s = 0; s < T::KS; ++s)
+        qf[s] = *reinterpret_cast<const u32x4*>(qs[rg] + col * T::ROW +
+                                               (((2 * s + g) ^ k_swz<D>(col)) * 16));
     for (int i = 0; i < steps; i += 2) {
         const int j = kp + T::KP * i;
         load(j + T::KP, ks1[kp], vs1[kp]);

@@ -482,9 +482,10 @@ hipError_t launch_pp(const void* q, const void* k, const void* v, void* o, float
 // most compute units idle. The key-split kernel (64-row work-groups whose key range runs in
 // four parts side by side) shortens that chain 4x but reads every K/V tile once per 64 rows
 // instead of once per 256. Measured (MI355X, us, ping-pong -> key-split): at 64 ping-pong
-// work-groups B2 H8 N1024 d64 causal 20.2 -> 10.2, B1 H8 N2048 d128 causal 43.3 -> 23.8; at
-// 128 B1 H8 N4096 d128 causal 82.2 -> 51.4, B1 H32 Hkv8 N1024 d128 25.9 -> 23.1, but B4 H8
-// N1024 d128 25.8 -> 27.1; at 256 B2 H16 N2048 d64 37.5 -> 39.1. The key-split kernel takes
+// work-groups B2 H8 N1024 d64 causal 20.3 -> 9.8, B1 H8 N2048 d128 causal 43.4 -> 22.7; at
+// 128 B1 H8 N4096 d128 causal 81.2 -> 49.5, B1 H32 Hkv8 N1024 d128 25.8 -> 20.1, B4 H8
+// N1024 d128 25.7 -> 24.4; at 256 (before the key-split kernel shared its Q tiles) B2 H16
+// N2048 d64 37.5 -> 39.1. The key-split kernel takes
 // launches of up to 128 ping-pong work-groups (half the compute units) whose key range is
 // longer than two 64-key tiles; with at most 128 keys there is no chain to split, and its
 // barrier and larger work-groups cost ~1 us (B2 H8 N128 d64 causal: 5.9 -> 6.3 us).
