@@ -47,7 +47,7 @@ extern "C" {
 typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID = -1,      /* an argument is out of its documented range           */
-    FA_ERR_UNSUPPORTED = -2,  /* a valid request this build does not implement        */
+    FA_ERR_UNSUPPORTED = -2,  /* a valid request the library does not implement      */
     FA_ERR_HIP = -3,          /* the HIP runtime reported an error at launch          */
     FA_ERR_SCRATCH = -4       /* fa_decode_paged_noalloc: request exceeds its scratch */
 } fa_status;
