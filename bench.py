@@ -504,6 +504,23 @@ def main(argv=None):
             "traffic": measured_traffic("kv_append", "kv_append")}
         del akn, avn, akc, avc
 
+        # Context, not part of the path: the rate the vendor's GEMM (torch.mm, hipBLASLt)
+        # reaches on a large square bf16 product on the same chip, in the same run. The
+        # chip lowers its clock under sustained matrix load, so this is the practical
+        # ceiling against which the attention kernels' fraction of the nominal peak reads.
+        log("[bench] context: bf16 GEMM rate (torch.mm)")
+        gemm = {}
+        for n in (8192, 16384):
+            ga = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+            gb = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+            gc = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+            m_ms = timed(lambda: torch.mm(ga, gb, out=gc), n=max(4, args.reps // 4))
+            m_tf = 2.0 * n ** 3 / (m_ms * 1e-3) / 1e12
+            gemm[f"{n}^3"] = {"ms_mean": round(m_ms, 4), "TFLOP/s": round(m_tf, 1),
+                              "frac_of_bf16_peak": round(m_tf / PEAK_BF16_TFLOPS, 4)}
+            del ga, gb, gc
+        out["context_gemm_bf16"] = gemm
+
     if args.calibrate_copy:
         n = 1 << 30
         a = torch.empty(n, dtype=torch.uint8, device=dev)

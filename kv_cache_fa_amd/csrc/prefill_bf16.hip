@@ -212,6 +212,32 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 for (int i = 0; i < 16; ++i)
                     if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sacc[kb][i] = -INFINITY;
         }
+        if constexpr (PASS == 1) {
+            // Fast path of the statistics pass: the exponentials against the current
+            // reference, without the row max. If this lane's share of the row sum grew by
+            // at most 128, none of them exceeds ~128 (the sum's rounding hides less than 128
+            // while it stays below 2^26), so no score lies more than 8 (log2 units) above
+            // the reference: the path below would keep the reference and add the same
+            // values in the same order. Otherwise (or while the reference is still -inf)
+            // the wave takes that path.
+            const float mb0 = m_used * scale_log2;
+            float l_new = l_part;
+#pragma unroll
+            for (int t = 0; t < T::PS; ++t) {
+                const int kb = t >> 1, base = (t & 1) * 8;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float p0 = fast_exp2(fmaf(sacc[kb][base + 2 * u], scale_log2, -mb0));
+                    const float p1 = fast_exp2(fmaf(sacc[kb][base + 2 * u + 1], scale_log2, -mb0));
+                    l_new += p0 + p1;
+                }
+            }
+            const bool ok = m_used != -INFINITY && l_new <= l_part + 128.f;
+            if (!__builtin_amdgcn_ballot_w64(!ok)) {
+                l_part = l_new;
+                return;
+            }
+        }
         // Every row attends key 0 (causal rows see the whole prefix), so after the first
         // tile the max is finite and no -inf - -inf can occur.
         if constexpr (PASS != 2) {

@@ -28,7 +28,10 @@
 //   barrier that ends it. 64 KiB of LDS, one work-group per CU.
 // * The reference max used for the exponentials only moves when the row max grows by
 //   more than 8 (log2 units); exponentials stay below 2^8 and the result is unchanged
-//   because softmax(x) = softmax(x - c) ("FlashAttention'ın Temelleri").
+//   because softmax(x) = softmax(x - c) ("FlashAttention'ın Temelleri"). The row max
+//   itself is only computed when the tile's exponentials against the current reference
+//   say it may have moved (a lane's share of them summing to more than 128; without a
+//   window).
 // * Causal: the work-group visits the key tiles its last row needs; a wave skips the
 //   tiles entirely in its rows' future, and only tiles crossing a wave's diagonal (or
 //   Nk) are masked.
@@ -333,6 +336,35 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
                         if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sacc[kb][i] = -INFINITY;
+            }
+        }
+        // Fast path: the exponentials against the current reference, without the row max.
+        // If this lane's share of the row sum grew by at most 128, none of them exceeds
+        // ~128 (the sum's rounding hides less than 128 while it stays below 2^26), so no
+        // score lies more than 8 (log2 units) above the reference: the path below would
+        // keep the reference and compute the same values, and the tile is done. Otherwise
+        // (or while the reference is still -inf) the wave takes that path. Not with a
+        // window: a row's first visited tile may hold only a few of its keys, and the low
+        // reference they set (a move needs a rise of more than 8) would fail the check on
+        // most later tiles (B1 H32 Hkv8 N32768, window (4096, 0): 1.80 -> 1.89 ms).
+        if constexpr (!WINDOW) {
+            const float mb0 = m_used * scale_log2;
+            float l_new = l_part;
+#pragma unroll
+            for (int t = 0; t < T::PS; ++t) {
+                const int kb = t >> 1, base = (t & 1) * 8;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float p0 = fast_exp2(fmaf(sacc[kb][base + 2 * u], scale_log2, -mb0));
+                    const float p1 = fast_exp2(fmaf(sacc[kb][base + 2 * u + 1], scale_log2, -mb0));
+                    pf[t][u] = pack_bf16x2(p0, p1);
+                    l_new += p0 + p1;
+                }
+            }
+            const bool ok = m_used != -INFINITY && l_new <= l_part + 128.f;
+            if (!__builtin_amdgcn_ballot_w64(!ok)) {
+                l_part = l_new;
+                return;
             }
         }
         // Without a window every row attends key 0, so after its first tile the max is
