@@ -30,8 +30,10 @@
 //   more than 8 (log2 units); exponentials stay below 2^8 and the result is unchanged
 //   because softmax(x) = softmax(x - c) ("FlashAttention'ın Temelleri"). The row max
 //   itself is only computed when the tile's exponentials against the current reference
-//   say it may have moved (a lane's share of them summing to more than 128; without a
-//   window).
+//   say it may have moved (a lane's share of them summing to more than 128). With a
+//   window, every rise moves the reference until a wave's first tile that all its rows
+//   see whole, so later tiles do not fail that check against a reference taken from a
+//   few keys.
 // * Causal: the work-group visits the key tiles its last row needs; a wave skips the
 //   tiles entirely in its rows' future, and only tiles crossing a wave's diagonal (or
 //   Nk) are masked.
@@ -343,11 +345,16 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         // ~128 (the sum's rounding hides less than 128 while it stays below 2^26), so no
         // score lies more than 8 (log2 units) above the reference: the path below would
         // keep the reference and compute the same values, and the tile is done. Otherwise
-        // (or while the reference is still -inf) the wave takes that path. Not with a
-        // window: a row's first visited tile may hold only a few of its keys, and the low
-        // reference they set (a move needs a rise of more than 8) would fail the check on
-        // most later tiles (B1 H32 Hkv8 N32768, window (4096, 0): 1.80 -> 1.89 ms).
-        if constexpr (!WINDOW) {
+        // (or while the reference is still -inf) the wave takes that path.
+        // With a window, a row's first visited tiles may hold only a few of its keys, and the
+        // low reference they give (a move needs a rise of more than 8) would fail the check
+        // on most later tiles. So until the wave's first tile that every one of its rows sees
+        // whole (jf0), and at it, any rise moves the reference (the -inf start moves anyway),
+        // and only after it may a tile take the fast path. A window unbounded on the left has
+        // jf0 = 0, where every reference is still -inf: it computes exactly what the causal
+        // kernel does.
+        const bool settled = !WINDOW || j > jf0;
+        if (settled) {
             const float mb0 = m_used * scale_log2;
             float l_new = l_part;
 #pragma unroll
@@ -377,7 +384,7 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
         mx = fmaxf(mx, xor32(mx));
         const float m_cand = fmaxf(m_used, mx);
-        const bool move = m_cand > m_used + tau_raw;
+        const bool move = m_cand > m_used + (settled ? tau_raw : 0.f);
         if (__builtin_amdgcn_ballot_w64(move)) {
             // Only rows whose max moved change their reference (alpha = 1 elsewhere), so
             // a row's arithmetic never depends on the other rows of the wave.
