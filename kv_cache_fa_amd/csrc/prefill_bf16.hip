@@ -35,7 +35,10 @@
 //   reference max used for the exponentials is only moved when the true max grows by
 //   more than 8 (log2 units); exponentials then stay below 2^8 and the result is
 //   unchanged, since softmax(x) = softmax(x - c) for any c ("FlashAttention'ın
-//   Temelleri").
+//   Temelleri"). The statistics pass computes a tile's max only when the tile's
+//   exponentials against the current reference say it may have moved (a lane's share of
+//   them summing to more than 128), as the single-pass kernel does, so the two agree bit
+//   for bit.
 // * Causal: key tiles entirely in a row block's future are never visited; only the
 //   tiles crossing the diagonal (and a ragged last tile) pay for masking. Work is
 //   ordered longest-first, and each XCD's work-groups share the same (batch, head)
