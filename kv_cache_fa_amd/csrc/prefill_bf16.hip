@@ -203,6 +203,10 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     };
 
     auto softmax_pv = [&](const int j, const char* vst, auto par, auto masked) {
+        // No fusing of a separate multiply and add into one FMA here (the compiler may do it
+        // or not depending on the code around): the row sum's rescale-then-add must round
+        // the same way in the single-pass kernel and the statistics pass.
+#pragma clang fp contract(off)
         f32x16 (&sacc)[T::KB] = sbuf[decltype(par)::value];
         if constexpr (decltype(masked)::value) {
             // key offset inside the tile of element (kb, i) is kb*32 + 8*(i/4) + 4g + i%4;

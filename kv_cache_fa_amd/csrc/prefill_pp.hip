@@ -316,6 +316,10 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 
     // Softmax phase of tile j: mask, running max (lazy reference), P = exp2 into pf.
     auto softmax_phase = [&](const int j) __attribute__((always_inline)) {
+        // No fusing of a separate multiply and add into one FMA here (the compiler may do it
+        // or not depending on the code around): the row sum's rescale-then-add must round
+        // the same way in the single-pass kernel and the statistics pass.
+#pragma clang fp contract(off)
         if (j < jf0 || j >= jf1) {
             // key offset inside the tile of element (kb, i) is kb*32 + 8*(i/4) + 4g + i%4;
             // it is dead past the row's last key and past Nk (and, for a window, before

@@ -2,6 +2,8 @@
 path through the C ABI, bring results back, compare with the oracle."""
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 from kv_cache_fa_amd import _lib, inputs
@@ -115,3 +117,23 @@ def check_fp32(o_got, lse_got, o_ref, lse_ref, what=""):
     assert mx <= FP32_MAX_ABS, msg
     assert lmx <= LSE_ABS, msg
     return mx, mean, lmx
+
+
+def shaped_scores(inp, pattern):
+    """Put a score profile along the keys into dimension 0 (q0 = 8 for every query): with
+    "rise" the score grows by ~0.4 (log2 units) per key, ~26 per 64-key tile, so the
+    reference max moves on every tile; with "step" every key from 64 on scores ~6 (log2
+    units) above keys 0..63, so against a reference taken in the first tile the
+    exponentials of a later tile sum far above 128 per lane while the max never rises by
+    8 (the reference stays). Other dimensions keep their N(0,1) draws."""
+    c = inp.cfg
+    q, k = inp.q.copy(), inp.k.copy()
+    unit = c.scale * math.log2(math.e) * 8.0          # log2 units per unit of k0
+    t = np.arange(c.Nk, dtype=np.float64)
+    if pattern == "rise":
+        k0 = np.minimum(t * 0.4 / unit, 120.0 / unit)  # scores stay below ~120 (log2 units)
+    else:
+        k0 = np.where(t >= 64, 6.0 / unit, 0.0)
+    q[..., 0] = inputs.f32_to_bf16_bits(np.full(q.shape[:-1], 8.0, np.float32))
+    k[..., 0] = inputs.f32_to_bf16_bits(np.broadcast_to(k0.astype(np.float32), k.shape[:-1]))
+    return inputs.PrefillInputs(c, q, k, inp.v, inp.rng)

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from kv_cache_fa_amd import inputs
-from gpu_helpers import check_bf16, check_fp32, run_prefill, widen_out
+from gpu_helpers import check_bf16, check_fp32, run_prefill, shaped_scores, widen_out
 
 pytestmark = pytest.mark.gpu
 
@@ -226,3 +226,17 @@ def test_lse_optional():
     o1, _ = run_prefill(inp, with_lse=False)
     o2, _ = run_prefill(inp, with_lse=True)
     assert np.array_equal(o1, o2)
+
+
+# ---- the running reference max: moves, and checks that fail without a move ------------
+@pytest.mark.parametrize("pattern", ["rise", "step"])
+@pytest.mark.parametrize("B,H,Hkv,N,causal", [
+    (2, 32, 8, 1024, True),    # 256 blocks of 256 rows: the ping-pong kernel
+    (2, 32, 8, 1024, False),
+    (1, 4, 2, 1000, True),     # 16 blocks: the key-split kernel
+])
+def test_reference_max_moves_and_stays(pattern, B, H, Hkv, N, causal):
+    base = inputs.custom_prefill(B, H, Hkv, N, N, 128, causal, "bf16", seed=61)
+    inp = shaped_scores(base, pattern)
+    rows = {(0, 0): np.arange(N), (B - 1, H - 1): np.arange(N)}
+    _sampled_check(inp, rows, f"reference max, {pattern}")

@@ -16,7 +16,8 @@ import pytest
 
 import oracle
 from kv_cache_fa_amd import _lib, inputs
-from gpu_helpers import BF16_MAX_ABS, bf16_from_dev, bf16_to_dev, check_bf16, errors
+from gpu_helpers import (BF16_MAX_ABS, bf16_from_dev, bf16_to_dev, check_bf16, errors,
+                         shaped_scores)
 
 pytestmark = pytest.mark.gpu
 
@@ -78,3 +79,25 @@ def test_two_pass_gqa_sampled():
     gl = np.concatenate([l2[b, h, idx] for (b, h), idx in rows.items()])
     wl = np.concatenate([L[key] for key in rows])
     check_bf16(got, gl, want, wl, "two-pass gqa sampled")
+
+
+@pytest.mark.parametrize("pattern", ["rise", "step"])
+def test_two_pass_reference_max_agrees_with_single_pass(pattern):
+    """Scores that move the reference max on every tile ("rise") or fail the max-free check
+    of the statistics pass without moving it ("step"): the statistics pass must still
+    reproduce the single pass's lse bit for bit (ping-pong launch), and both outputs
+    must meet the oracle."""
+    base = inputs.custom_prefill(1, 256, 32, 300, 700, 128, True, seed=63)
+    inp = shaped_scores(base, pattern)
+    _say(f"[two-pass] reference max, {pattern}")
+    o2, l2, o1, l1 = run_both(inp)
+    assert np.array_equal(l2, l1), "statistics pass lse differs from the single pass"
+    rows = {(0, 0): np.arange(300), (0, 255): np.arange(300)}
+    q, k, v = inp.as_f64()
+    Or, Lr = oracle.attention(q, k, v, causal=True, scale=inp.cfg.scale, rows=rows)
+    for o_h, l_h, what in ((o2, l2, "two-pass"), (o1, l1, "single pass")):
+        got = np.concatenate([inputs.bf16_bits_to_f64(o_h[b, h, idx]) for (b, h), idx in rows.items()])
+        want = np.concatenate([Or[x] for x in rows])
+        lg = np.concatenate([l_h[b, h, idx] for (b, h), idx in rows.items()])
+        lw = np.concatenate([Lr[x] for x in rows])
+        check_bf16(got, lg, want, lw, f"{what}, reference max {pattern}")

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from kv_cache_fa_amd import _lib, inputs
-from gpu_helpers import bf16_from_dev, bf16_to_dev, check_bf16
+from gpu_helpers import bf16_from_dev, bf16_to_dev, check_bf16, shaped_scores
 
 pytestmark = pytest.mark.gpu
 
@@ -125,3 +125,24 @@ def test_window_benched_workload_sampled():
     gl = np.concatenate([lse_h[b, h, idx] for (b, h), idx in rows.items()])
     wl = np.concatenate([L[key] for key in rows])
     check_bf16(got, gl, want, wl, "window benched workload")
+
+
+@pytest.mark.parametrize("pattern", ["rise", "step"])
+@pytest.mark.parametrize("left,right", [(300, 0), (100, 40), (700, 0)])
+def test_window_reference_max(pattern, left, right):
+    """Scores rising along the keys, or stepping up after the first 64 keys: rows start
+    their windows mid-tile, where any rise moves the reference, and later tiles may take
+    the max-free path. Every row of two heads against the oracle."""
+    base = inputs.custom_prefill(2, 32, 8, 1024, 1024, 128, False, seed=64 + left + right)
+    inp = shaped_scores(base, pattern)
+    _say(f"[window] reference max {pattern} ({left},{right})")
+    o_h, lse_h = run_window(inp, left, right)
+    rows = {(0, 0): np.arange(1024), (1, 31): np.arange(1024)}
+    q, k, v = inp.as_f64()
+    O, L = oracle.attention(q, k, v, causal=False, scale=inp.cfg.scale, rows=rows,
+                            window=(left, right))
+    got = np.concatenate([inputs.bf16_bits_to_f64(o_h[b, h, idx]) for (b, h), idx in rows.items()])
+    want = np.concatenate([O[key] for key in rows])
+    gl = np.concatenate([lse_h[b, h, idx] for (b, h), idx in rows.items()])
+    wl = np.concatenate([L[key] for key in rows])
+    check_bf16(got, gl, want, wl, f"window ({left},{right}) reference max {pattern}")
