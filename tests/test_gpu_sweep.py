@@ -14,7 +14,8 @@ import pytest
 
 import oracle
 from kv_cache_fa_amd import _lib, inputs
-from gpu_helpers import bf16_from_dev, bf16_to_dev, check_bf16, run_decode, run_prefill
+from gpu_helpers import (bf16_from_dev, bf16_to_dev, check_bf16, run_decode, run_prefill,
+                         shaped_scores, widen_out)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +37,26 @@ def _prefill_cases(n, seed):
         Nq = int(rng.integers(1, 700))
         Nk = Nq + int(rng.integers(0, 500)) if causal else int(rng.integers(1, 900))
         out.append((B, H, Hkv, Nq, Nk, d, causal))
+    return out
+
+
+def _ping_pong_cases(n, seed):
+    """Shapes that fa_fwd runs on the ping-pong kernel (more than 128 blocks of 256 rows),
+    with a score profile each: plain N(0,1), Q four times larger (peaky rows), scores
+    rising along the keys, or stepping up after the first 64 keys."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([4, 8, 16, 32]))
+        H = Hkv * int(rng.choice([1, 2, 4, 8]))
+        causal = bool(rng.integers(0, 2))
+        Nq = int(rng.integers(129, 1300))
+        Nk = Nq + int(rng.integers(0, 700)) if causal else int(rng.integers(1, 1500))
+        B = int(rng.integers(1, 3))
+        while -(-Nq // 256) * B * H <= 128:
+            H *= 2
+        out.append((B, H, Hkv, Nq, Nk, d, causal, str(rng.choice(["plain", "x4", "rise", "step"]))))
     return out
 
 
@@ -89,6 +110,31 @@ def test_sweep_prefill(shape):
     q, k, v = inp.as_f64()
     O, L = oracle.attention(q, k, v, causal=causal, scale=inp.cfg.scale)
     check_bf16(inputs.bf16_bits_to_f64(o_h), lse_h, O, L, f"sweep prefill {shape}")
+
+
+@pytest.mark.parametrize("shape", _ping_pong_cases(24, 2028), ids=lambda s: str(s))
+def test_sweep_prefill_ping_pong(shape):
+    """Every row of two seeded (batch, head) pairs against the oracle."""
+    B, H, Hkv, Nq, Nk, d, causal, pattern = shape
+    base = inputs.custom_prefill(B, H, Hkv, Nq, Nk, d, causal, "bf16", seed=Nq + Nk + d + H)
+    if pattern in ("rise", "step"):
+        inp = shaped_scores(base, pattern)
+    elif pattern == "x4":
+        q = inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(base.q) * np.float32(4.0))
+        inp = inputs.PrefillInputs(base.cfg, q, base.k, base.v, base.rng)
+    else:
+        inp = base
+    _say(f"[sweep] ping-pong prefill {shape}")
+    o_h, lse_h = run_prefill(inp)
+    rng = np.random.default_rng(Nq * 7 + Nk)
+    rows = {(int(rng.integers(0, B)), int(rng.integers(0, H))): np.arange(Nq) for _ in range(2)}
+    qf, kf, vf = inp.as_f64()
+    O, L = oracle.attention(qf, kf, vf, causal=causal, scale=inp.cfg.scale, rows=rows)
+    got = np.concatenate([widen_out(o_h[b, h, idx], "bf16") for (b, h), idx in rows.items()])
+    want = np.concatenate([O[x] for x in rows])
+    lg = np.concatenate([lse_h[b, h, idx] for (b, h), idx in rows.items()])
+    lw = np.concatenate([L[x] for x in rows])
+    check_bf16(got, lg, want, lw, f"sweep ping-pong {shape}")
 
 
 @pytest.mark.parametrize("shape", _window_cases(16, 2025), ids=lambda s: str(s))
