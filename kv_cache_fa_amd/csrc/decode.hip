@@ -33,9 +33,13 @@
 //   and come back as the A operand through transposing reads (ds_read_b64_tr_b16). The
 //   accumulator is 4 fp32 per 16 dims per lane whatever the head count (a 16-head group
 //   held 128 per lane on FMAs, one wave per SIMD).
-// * P.V otherwise (e4m3 cache, KV head pairs): plain FMAs. A lane owns one 16-byte chunk
+// * P.V otherwise (e4m3 cache, KV head pairs): on the VALU. A lane owns one 16-byte chunk
 //   of V rows (8 dims) for a subset of the page's tokens and accumulates all heads of the
-//   group; the probabilities reach it through a small per-wave LDS table.
+//   group; the probabilities reach it through a small per-wave LDS table. With KV head
+//   pairs (256-element rows) the lane takes its tokens two at a time: each dim's two values
+//   and the two probabilities (rounded to bf16, as the matrix-unit paths round them) form
+//   bf16 pairs, and one v_dot2c_f32_bf16 adds both products to the fp32 accumulator (half
+//   the instructions of fp32 FMAs); otherwise plain FMAs.
 // * A segment's partial result (normalised O_k, lse_k in log2 units) goes to the
 //   caller's workspace, slot k = its work-group's index among those covering the
 //   sequence; a second kernel merges a sequence's slots in order.
@@ -114,6 +118,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     constexpr int KDMA = PAGEB / 1024;             // 1 KiB direct loads per page
     static_assert(KDMA >= 1 && KDMA * 1024 == PAGEB, "whole 1 KiB loads per page");
     constexpr bool MPV = MMA;                      // P.V on the matrix unit
+    // KV head pairs with 256-element rows (two token groups): P.V by v_dot2c_f32_bf16, two
+    // tokens of one dim per instruction (the lane's tokens tg + 2i come in pairs 4 ip + tg,
+    // 4 ip + tg + 2, both held by one score lane).
+    constexpr bool DOT = PAIR && TG == 2;
+    static_assert(!DOT || TPL == 8, "dot2 P.V: eight tokens per lane");
     static_assert(!MMA || (!FP8 && !PAIR), "matrix-unit P.V: bf16 cache, one KV head");
     constexpr int VB = D / 16;                     // 16-dim blocks of O^T (MPV)
     // Per wave: two K stages (separate arrays, so the compiler can tell a read of one from
@@ -141,7 +150,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
             return red_o_x + (ww * GH + hh) * D;
         }
     };
-    __shared__ float p_lds[kWaves][MPV ? 1 : kPage][MPV ? 1 : GH];
+    __shared__ float p_lds[kWaves][MPV || DOT ? 1 : kPage][MPV || DOT ? 1 : GH];
+    // DOT: the probabilities of tokens (4 q + r, 4 q + r + 2), r = 0, 1, as bf16 pairs.
+    __shared__ __attribute__((aligned(16))) uint32_t p2_lds[kWaves][DOT ? kPage / 2 : 1][DOT ? GH : 1];
     __shared__ float a_lds[kWaves][GH];
     __shared__ float red_m[kWaves][GH];
     __shared__ float red_l[kWaves][GH];
@@ -368,11 +379,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
                 }
                 return;
             }
+            float pq[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float p = fast_exp2(fmaf(acc[i], scale_log2, -mb));
-                l_part += p;
-                if (n < GH) p_lds[w][kq * 4 + i][n] = p;
+                l_part += p;  // the row sum takes the unrounded values
+                pq[i] = p;
+                if constexpr (!DOT)
+                    if (n < GH) p_lds[w][kq * 4 + i][n] = p;
+            }
+            if constexpr (DOT) {
+                if (n < GH) {
+                    p2_lds[w][2 * kq][n] = pack_bf16x2(pq[0], pq[2]);
+                    p2_lds[w][2 * kq + 1][n] = pack_bf16x2(pq[1], pq[3]);
+                }
             }
             wave_lds_fence();
 
@@ -383,6 +403,51 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
                     for (int e = 0; e < 8; ++e) oacc[hh][e] *= a;
                 }
+            }
+            if constexpr (DOT) {
+                // Tokens a = 4 ip + tg and b = a + 2 (the lane's VV[2 ip], VV[2 ip + 1]): each
+                // dim's two values become one bf16 pair, and one v_dot2c per (dim, head)
+                // adds p_a v_a + p_b v_b to the fp32 accumulator.
+#pragma unroll
+                for (int ip = 0; ip < TPL / 2; ++ip) {
+                    const int ta = tg + TG * (2 * ip);
+                    const bool oka = tok0 + ta < t1, okb = tok0 + ta + TG < t1;  // past the
+                    uint32_t wa[4], wb[4];  // sequence: zeros (slots may hold anything)
+                    if constexpr (FP8) {
+                        const u32x2 a0 = fp8x4_to_bf16x4(oka ? VV[2 * ip][0] : 0u);
+                        const u32x2 a1 = fp8x4_to_bf16x4(oka ? VV[2 * ip][1] : 0u);
+                        const u32x2 b0 = fp8x4_to_bf16x4(okb ? VV[2 * ip + 1][0] : 0u);
+                        const u32x2 b1 = fp8x4_to_bf16x4(okb ? VV[2 * ip + 1][1] : 0u);
+                        wa[0] = a0[0]; wa[1] = a0[1]; wa[2] = a1[0]; wa[3] = a1[1];
+                        wb[0] = b0[0]; wb[1] = b0[1]; wb[2] = b1[0]; wb[3] = b1[1];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            wa[e] = oka ? VV[2 * ip][e] : 0u;
+                            wb[e] = okb ? VV[2 * ip + 1][e] : 0u;
+                        }
+                    }
+                    const u32x4 pp = *reinterpret_cast<const u32x4*>(&p2_lds[w][2 * ip + tg][kc * G2]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        // (a, b) of dims 2e and 2e + 1: low halves, high halves
+                        const uint32_t lo = __builtin_amdgcn_perm(wb[e], wa[e], 0x05040100u);
+                        const uint32_t hi = __builtin_amdgcn_perm(wb[e], wa[e], 0x07060302u);
+#pragma unroll
+                        for (int hh = 0; hh < G2; ++hh) {
+                            // (through a scalar: this compiler bit-casts a vector element
+                            // taken in place as element 0)
+                            const uint32_t pw = pp[hh];
+                            const bf16x2 ph = __builtin_bit_cast(bf16x2, pw);
+                            oacc[hh][2 * e] = __builtin_amdgcn_fdot2_f32_bf16(
+                                __builtin_bit_cast(bf16x2, lo), ph, oacc[hh][2 * e], false);
+                            oacc[hh][2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+                                __builtin_bit_cast(bf16x2, hi), ph, oacc[hh][2 * e + 1], false);
+                        }
+                    }
+                }
+                wave_lds_fence();
+                return;
             }
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
