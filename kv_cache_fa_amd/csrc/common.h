@@ -53,15 +53,6 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
     const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
     return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
-// Four e4m3 bytes -> four fp32.
-__device__ __forceinline__ void fp8x4_to_f32x4(uint32_t w, float* x) {
-    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-    x[0] = lo[0];
-    x[1] = lo[1];
-    x[2] = hi[0];
-    x[3] = hi[1];
-}
 
 // 16 bytes per lane from a buffer straight into LDS: lane L writes lds_base + 16 L
 // (buffer_load_dwordx4 ... lds). lds_base must be the same in all lanes; loads past the

@@ -35,11 +35,12 @@
 //   held 128 per lane on FMAs, one wave per SIMD).
 // * P.V otherwise (e4m3 cache, KV head pairs): on the VALU. A lane owns one 16-byte chunk
 //   of V rows (8 dims) for a subset of the page's tokens and accumulates all heads of the
-//   group; the probabilities reach it through a small per-wave LDS table. With KV head
-//   pairs (256-element rows) the lane takes its tokens two at a time: each dim's two values
-//   and the two probabilities (rounded to bf16, as the matrix-unit paths round them) form
-//   bf16 pairs, and one v_dot2c_f32_bf16 adds both products to the fp32 accumulator (half
-//   the instructions of fp32 FMAs); otherwise plain FMAs.
+//   group; the probabilities reach it through a small per-wave LDS table. The lane takes
+//   its tokens two at a time: each dim's two values and the two probabilities (rounded to
+//   bf16, as the matrix-unit paths round them) form bf16 pairs, and one v_dot2c_f32_bf16
+//   adds both products to the fp32 accumulator (half the instructions of fp32 FMAs). With
+//   KV head pairs (256-element rows) one score lane produces both tokens of a pair, so the
+//   table holds the probabilities already paired.
 // * A segment's partial result (normalised O_k, lse_k in log2 units) goes to the
 //   caller's workspace, slot k = its work-group's index among those covering the
 //   sequence; a second kernel merges a sequence's slots in order.
@@ -123,6 +124,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     // 4 ip + tg + 2, both held by one score lane).
     constexpr bool DOT = PAIR && TG == 2;
     static_assert(!DOT || TPL == 8, "dot2 P.V: eight tokens per lane");
+    // The other VALU P.V layouts pair the lane's tokens tg + TG (2 ip) and tg + TG (2 ip + 1),
+    // which different score lanes produce: the probabilities stay fp32 in LDS and the P.V
+    // lane packs each pair itself.
+    static_assert(MPV || TPL % 2 == 0, "dot2 P.V: an even number of tokens per lane");
     static_assert(!MMA || (!FP8 && !PAIR), "matrix-unit P.V: bf16 cache, one KV head");
     constexpr int VB = D / 16;                     // 16-dim blocks of O^T (MPV)
     // Per wave: two K stages (separate arrays, so the compiler can tell a read of one from
@@ -150,7 +155,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
             return red_o_x + (ww * GH + hh) * D;
         }
     };
-    __shared__ float p_lds[kWaves][MPV || DOT ? 1 : kPage][MPV || DOT ? 1 : GH];
+    __shared__ float p_lds[kWaves][MPV || DOT ? 1 : kPage][MPV || DOT ? 1 : GH];  // fp32 P
     // DOT: the probabilities of tokens (4 q + r, 4 q + r + 2), r = 0, 1, as bf16 pairs.
     __shared__ __attribute__((aligned(16))) uint32_t p2_lds[kWaves][DOT ? kPage / 2 : 1][DOT ? GH : 1];
     __shared__ float a_lds[kWaves][GH];
@@ -404,10 +409,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
                     for (int e = 0; e < 8; ++e) oacc[hh][e] *= a;
                 }
             }
-            if constexpr (DOT) {
-                // Tokens a = 4 ip + tg and b = a + 2 (the lane's VV[2 ip], VV[2 ip + 1]): each
-                // dim's two values become one bf16 pair, and one v_dot2c per (dim, head)
-                // adds p_a v_a + p_b v_b to the fp32 accumulator.
+            {
+                // Tokens a = tg + TG (2 ip) and b = a + TG (the lane's VV[2 ip], VV[2 ip + 1];
+                // with pairs 4 ip + tg and 4 ip + tg + 2): each dim's two values become one
+                // bf16 pair, and one v_dot2c per (dim, head) adds p_a v_a + p_b v_b to the
+                // fp32 accumulator.
 #pragma unroll
                 for (int ip = 0; ip < TPL / 2; ++ip) {
                     const int ta = tg + TG * (2 * ip);
@@ -427,7 +433,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
                             wb[e] = okb ? VV[2 * ip + 1][e] : 0u;
                         }
                     }
-                    const u32x4 pp = *reinterpret_cast<const u32x4*>(&p2_lds[w][2 * ip + tg][kc * G2]);
+                    uint32_t pp[G2];  // bf16 pairs (p_a, p_b) of the lane's heads
+                    if constexpr (DOT) {
+                        // (element by element into the array: this compiler bit-casts a vector
+                        // element taken in place as element 0)
+                        const u32x4 p4 = *reinterpret_cast<const u32x4*>(&p2_lds[w][2 * ip + tg][kc * G2]);
+#pragma unroll
+                        for (int hh = 0; hh < G2; ++hh) pp[hh] = p4[hh];
+                    } else {
+#pragma unroll
+                        for (int hh = 0; hh < G2; ++hh)
+                            pp[hh] = pack_bf16x2(p_lds[w][ta][kc * G2 + hh],
+                                                 p_lds[w][ta + TG][kc * G2 + hh]);
+                    }
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         // (a, b) of dims 2e and 2e + 1: low halves, high halves
@@ -435,10 +453,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
                         const uint32_t hi = __builtin_amdgcn_perm(wb[e], wa[e], 0x07060302u);
 #pragma unroll
                         for (int hh = 0; hh < G2; ++hh) {
-                            // (through a scalar: this compiler bit-casts a vector element
-                            // taken in place as element 0)
-                            const uint32_t pw = pp[hh];
-                            const bf16x2 ph = __builtin_bit_cast(bf16x2, pw);
+                            const bf16x2 ph = __builtin_bit_cast(bf16x2, pp[hh]);
                             oacc[hh][2 * e] = __builtin_amdgcn_fdot2_f32_bf16(
                                 __builtin_bit_cast(bf16x2, lo), ph, oacc[hh][2 * e], false);
                             oacc[hh][2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(
@@ -447,32 +462,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
                     }
                 }
                 wave_lds_fence();
-                return;
             }
-#pragma unroll
-            for (int i = 0; i < TPL; ++i) {
-                const int tl = tg + TG * i;
-                const bool ok = tok0 + tl < t1;  // slots past the sequence may hold anything
-                float x[8];
-                if constexpr (FP8) {
-                    fp8x4_to_f32x4(ok ? VV[i][0] : 0u, x);
-                    fp8x4_to_f32x4(ok ? VV[i][1] : 0u, x + 4);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t wd = ok ? VV[i][e] : 0u;
-                        x[2 * e] = bf16lo(wd);
-                        x[2 * e + 1] = bf16hi(wd);
-                    }
-                }
-#pragma unroll
-                for (int hh = 0; hh < G2; ++hh) {
-                    const float p = p_lds[w][tl][kc * G2 + hh];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) oacc[hh][e] = fmaf(p, x[e], oacc[hh][e]);
-                }
-            }
-            wave_lds_fence();
         }
     };
     for (int it = 0; it < n_my; it += 2) {
