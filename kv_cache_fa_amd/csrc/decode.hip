@@ -33,6 +33,9 @@
 //   and come back as the A operand through transposing reads (ds_read_b64_tr_b16). The
 //   accumulator is 4 fp32 per 16 dims per lane whatever the head count (a 16-head group
 //   held 128 per lane on FMAs, one wave per SIMD).
+// * The same on an e4m3 cache with d = 128 and groups of more than 4 heads: the V rows
+//   come through registers (as below), are converted exactly to bf16 and written into the
+//   bf16 stage right before their P.V.
 // * P.V otherwise (e4m3 cache, KV head pairs): on the VALU. A lane owns one 16-byte chunk
 //   of V rows (8 dims) for a subset of the page's tokens and accumulates all heads of the
 //   group; the probabilities reach it through a small per-wave LDS table. The lane takes
@@ -128,29 +131,40 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     // which different score lanes produce: the probabilities stay fp32 in LDS and the P.V
     // lane packs each pair itself.
     static_assert(MPV || TPL % 2 == 0, "dot2 P.V: an even number of tokens per lane");
-    static_assert(!MMA || (!FP8 && !PAIR), "matrix-unit P.V: bf16 cache, one KV head");
+    static_assert(!MMA || !PAIR, "matrix-unit P.V: one KV head");
+    static_assert(!MMA || !FP8 || D == 128, "matrix-unit P.V on an e4m3 cache: d = 128");
     constexpr int VB = D / 16;                     // 16-dim blocks of O^T (MPV)
+    // MPV: the V stage holds bf16 rows. A bf16 cache's pages go there by direct loads; an
+    // e4m3 cache's V rows come through registers (as for the VALU P.V) and are converted
+    // into the stage just before their P.V.
+    constexpr int VROWB = MPV ? D * 2 : ROWB;      // bytes of one V stage row
+    constexpr int VPAGEB = kPage * VROWB;          // bytes of one V stage
+    constexpr bool VDMA = MPV && !FP8;             // V by direct loads into the stage
     // Per wave: two K stages (separate arrays, so the compiler can tell a read of one from
     // the direct loads into the other); after the wave's loop its partial output for the
     // cross-wave merge reuses the first stage when it fits.
     __shared__ __attribute__((aligned(1024))) char kst_a[kWaves][PAGEB];
     __shared__ __attribute__((aligned(1024))) char kst_b[kWaves][PAGEB];
-    // V stages of the matrix-unit P.V (same shape as the K stages).
-    __shared__ __attribute__((aligned(1024))) char vst_a[kWaves][MPV ? PAGEB : 16];
-    __shared__ __attribute__((aligned(1024))) char vst_b[kWaves][MPV ? PAGEB : 16];
+    // V stages of the matrix-unit P.V (bf16 rows).
+    __shared__ __attribute__((aligned(1024))) char vst_a[kWaves][MPV ? VPAGEB : 16];
+    __shared__ __attribute__((aligned(1024))) char vst_b[kWaves][MPV ? VPAGEB : 16];
     // The waves' partial outputs [GH][D] for the cross-wave merge: in the first K stage
-    // when they fit, with MPV in both K stages (rows of heads [0, HPS) in the first),
-    // else in an array of their own.
+    // when they fit, with MPV in both K stages or (e4m3, whose K stages are the smaller
+    // ones) both V stages (rows of heads [0, HPS) in the first), else in an array of their
+    // own.
     constexpr bool RO_IN_A = GH * D * 4 <= PAGEB;
     constexpr bool RO_IN_AB = MPV && !RO_IN_A;
-    static_assert(!RO_IN_AB || GH * D * 4 <= 2 * PAGEB, "two K stages hold the partial output");
+    constexpr int RO_STAGE = FP8 ? VPAGEB : PAGEB;  // bytes of each stage the merge uses
+    static_assert(!RO_IN_AB || GH * D * 4 <= 2 * RO_STAGE, "two stages hold the partial output");
     __shared__ float red_o_x[RO_IN_A || RO_IN_AB ? 1 : kWaves * GH * D];
     auto red_o_row = [&](int ww, int hh) -> float* {  // head hh's D floats of wave ww
         if constexpr (RO_IN_A) {
             return reinterpret_cast<float*>(kst_a[ww]) + hh * D;
         } else if constexpr (RO_IN_AB) {
-            constexpr int HPS = PAGEB / (D * 4);
-            return reinterpret_cast<float*>(hh < HPS ? kst_a[ww] : kst_b[ww]) + (hh % HPS) * D;
+            constexpr int HPS = RO_STAGE / (D * 4);
+            char* const first = FP8 ? vst_a[ww] : kst_a[ww];
+            char* const second = FP8 ? vst_b[ww] : kst_b[ww];
+            return reinterpret_cast<float*>(hh < HPS ? first : second) + (hh % HPS) * D;
         } else {
             return red_o_x + (ww * GH + hh) * D;
         }
@@ -211,30 +225,32 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         const int b = (32 * j + 8 * kq) * ES;
         kr_off[j] = n * ROWB + (((b / 16) ^ (n % KCH)) * 16) + b % 16;
     }
-    // MPV: V stage rows are tokens of ROWB bytes, 16-byte chunks XOR-swizzled by row so that
+    // MPV: V stage rows are tokens of VROWB bytes, 16-byte chunks XOR-swizzled by row so that
     // a transposing read (16-lane group kq: tokens 4 kq + e, e = 0..3, 8 bytes of dims
     // 16 vb + 4 a each) and its neighbour group (tokens 4 kq + 4 + e), which the LDS serves
     // together, hit 32 different bank pairs.
     auto v_swz_dec = [](int r) -> int {
-        if constexpr (ROWB == 256) return 4 * (r & 3) + 2 * ((r >> 2) & 1);
+        if constexpr (VROWB == 256) return 4 * (r & 3) + 2 * ((r >> 2) & 1);
         else return 2 * ((r >> 1) & 3);
     };
-    static_assert(!MPV || ROWB == 256 || ROWB == 128, "MPV: d = 128 or 64");
-    uint32_t vd_off[MPV ? KDMA : 1];
+    static_assert(!MPV || VROWB == 256 || VROWB == 128, "MPV: d = 128 or 64");
+    uint32_t vd_off[VDMA ? KDMA : 1];
     int vr_off[MPV ? VB : 1];
     if constexpr (MPV) {
+        if constexpr (VDMA) {
 #pragma unroll
-        for (int i = 0; i < KDMA; ++i) {
-            const int byte = 1024 * i + 16 * lane;
-            const int r = byte / ROWB, pc = (byte % ROWB) / 16;
-            vd_off[i] = (uint32_t)(r * tok_stride * ES + ((pc ^ v_swz_dec(r)) * 16));
+            for (int i = 0; i < KDMA; ++i) {
+                const int byte = 1024 * i + 16 * lane;
+                const int r = byte / VROWB, pc = (byte % VROWB) / 16;
+                vd_off[i] = (uint32_t)(r * tok_stride * ES + ((pc ^ v_swz_dec(r)) * 16));
+            }
         }
         // Source lane a + 4 e of group kq points at token 4 kq + e, dims 16 vb + 4 a .. +3:
         // logical chunk 2 vb + a / 2, byte 8 (a % 2) in it.
         const int va = lane & 3, vrow = 4 * kq + ((lane >> 2) & 3);
 #pragma unroll
         for (int vb = 0; vb < VB; ++vb)
-            vr_off[vb] = vrow * ROWB + (((2 * vb + (va >> 1)) ^ v_swz_dec(vrow)) * 16) + 8 * (va & 1);
+            vr_off[vb] = vrow * VROWB + (((2 * vb + (va >> 1)) ^ v_swz_dec(vrow)) * 16) + 8 * (va & 1);
     }
     char* const kst0 = kst_a[w];
     char* const kst1 = kst_b[w];
@@ -294,7 +310,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         }
 #pragma unroll
         for (int i = 0; i < KDMA; ++i) buf_load16_lds_nt(rk, kst + 1024 * i, kd_off[i], 0u);
-        if constexpr (MPV) {
+        if constexpr (VDMA) {
             // V rows past the sequence's last token may hold anything; the descriptor ends
             // at the page's last valid row, so they arrive as zeros (0 x NaN would poison
             // the product even with a zero probability).
@@ -318,11 +334,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     // Every load of the page before this one's successor has landed: its K rows in LDS
     // (direct loads are counted by vmcnt only) and its V registers (MPV: V rows in LDS).
     auto wait_page = [&]() __attribute__((always_inline)) {
-        constexpr int later = KDMA + (MPV ? KDMA : TPL);  // loads of the page issued after it
+        constexpr int later = KDMA + (VDMA ? KDMA : TPL);  // loads of the page issued after it
         static_assert(later < 64, "vmcnt field");
         __builtin_amdgcn_s_waitcnt((later & 15) | ((later >> 4) << 14) | (7 << 4) | (15 << 8));
     };
-    auto page_compute = [&](const char* KST, const KVec (&VV)[TPL], const char* VST, const bool OK,
+    auto page_compute = [&](const char* KST, const KVec (&VV)[TPL], char* VST, const bool OK,
                             const int IT) {
         if (OK) {
             const int tok0 = (first_page + w + kWaves * IT) * kPage;
@@ -362,6 +378,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
             }
             const float mb = m_used * scale_log2;
             if constexpr (MPV) {
+                if constexpr (FP8) {
+                    // This page's V rows into the bf16 stage (e4m3 converted exactly; zeros
+                    // past the sequence): lane (tg, c) writes tokens tg + TG i, chunk c.
+#pragma unroll
+                    for (int i = 0; i < TPL; ++i) {
+                        const int tl = tg + TG * i;
+                        const bool ok = tok0 + tl < t1;
+                        const u32x2 lo = fp8x4_to_bf16x4(ok ? VV[i][0] : 0u);
+                        const u32x2 hi = fp8x4_to_bf16x4(ok ? VV[i][1] : 0u);
+                        *reinterpret_cast<u32x4*>(VST + tl * VROWB + ((c ^ v_swz_dec(tl)) * 16)) =
+                            u32x4{lo[0], lo[1], hi[0], hi[1]};
+                    }
+                    wave_lds_fence();  // the transposing reads take other lanes' rows
+                }
                 // P^T as the B operand: this lane's column n, tokens 4 kq .. 4 kq + 3 (bf16;
                 // the row sum takes the unrounded values).
                 float p[4];
@@ -778,12 +808,13 @@ DecodeWorkspace decode_workspace(void* ws, int num_seqs, int H, int d, int max_s
 
 // Work-groups aimed at: one round of resident ones (two for an fp8 cache, whose ranges take
 // half the time) shared by the (KV head, head group) pairs: 256 CUs (MI355X) times the
-// work-groups a CU holds. FMA P.V: by register use, 3 for 4 heads per group, 2 for 8, 1 for
-// 16. Matrix-unit P.V: by LDS (four K/V page stages per wave), 2 for d = 128 (66 KiB
-// each), 4 for d = 64. (Fixed numbers: no runtime query precedes the launch.)
+// work-groups a CU holds. VALU P.V: by register use, 3 for 4 heads per group, 2 for 8, 1
+// for 16. Matrix-unit P.V: by LDS (four K/V page stages per wave), 2 for d = 128 (66 KiB
+// each), 4 for d = 64, 3 for an e4m3 cache (its K stages are half the size: 49 KiB).
+// (Fixed numbers: no runtime query precedes the launch.)
 constexpr int kCUs = 256;
 int decode_target(int GH, bool mma, int groups, int d, bool fp8) {
-    const int per_cu = mma ? (d == 128 ? 2 : 4) : GH == 4 ? 3 : GH == 8 ? 2 : 1;
+    const int per_cu = mma ? (fp8 ? 3 : d == 128 ? 2 : 4) : GH == 4 ? 3 : GH == 8 ? 2 : 1;
     return std::max(1, per_cu * kCUs * (fp8 ? 2 : 1) / groups);
 }
 // Pairs: one round of the pair kernel's work-groups per CU (3 for bf16 with d = 64, else 2,
@@ -829,17 +860,17 @@ hipError_t launch_split_d(int GH, bool pair, bool mma, const void* q, const void
             return launch_split<D, 8, FP8, true>(q, kc, vc, pt, sl, ws, plan, target, rows,
                                                   num_seqs, H, Hkv, g, n_hg, num_pages,
                                                   max_pages, max_seq_len, scale, ks, vs, stream);
-    if constexpr (!FP8)
+    if constexpr (!FP8 || D == 128)
         if (mma) {
             if (GH == 4)
-                return launch_split<D, 4, false, false, true>(
+                return launch_split<D, 4, FP8, false, true>(
                     q, kc, vc, pt, sl, ws, plan, target, rows, num_seqs, H, Hkv, g, n_hg,
                     num_pages, max_pages, max_seq_len, scale, ks, vs, stream);
             if (GH == 8)
-                return launch_split<D, 8, false, false, true>(
+                return launch_split<D, 8, FP8, false, true>(
                     q, kc, vc, pt, sl, ws, plan, target, rows, num_seqs, H, Hkv, g, n_hg,
                     num_pages, max_pages, max_seq_len, scale, ks, vs, stream);
-            return launch_split<D, 16, false, false, true>(
+            return launch_split<D, 16, FP8, false, true>(
                 q, kc, vc, pt, sl, ws, plan, target, rows, num_seqs, H, Hkv, g, n_hg, num_pages,
                 max_pages, max_seq_len, scale, ks, vs, stream);
         }
@@ -892,12 +923,15 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
     // pairs would halve them (1 x 8192 tokens, H32 Hkv8 d128: 15.3 us single, 16.6 paired).
     const bool pair = (d * (fp8 ? 1 : 2) == 128 || (!fp8 && d == 128)) && Hkv % 2 == 0 &&
                       g <= 4 && num_seqs >= 32;
+    // An e4m3 cache with d = 128 and groups of more than 4 heads: P.V on the matrix unit
+    // too (64 x U{512..8192}: H32 Hkv4 84.7 -> 74.4 us, H32 Hkv2 89.7 -> 59.6 us against the
+    // VALU kernel, which holds every head's accumulators).
     // Single KV heads of a bf16 cache: P.V on the matrix unit, except for groups of up to 4
     // heads over 32 or more sequences, where the FMA kernel's third resident work-group per
     // CU (the matrix-unit kernel's V stages leave room for two) reads faster (64 x U{512..8192},
     // H28 Hkv7: 177.6 us on FMAs, 200.4 us on the matrix unit; 16 x 1024, H32 Hkv8: 22.7 vs
     // 16.9 us; 64 x U{512..8192}, H32 Hkv2: 93.2 vs 65.2 us).
-    const bool mma = !fp8 && !pair && (GH >= 8 || num_seqs < 32);
+    const bool mma = !pair && (fp8 ? d == 128 && GH >= 8 : GH >= 8 || num_seqs < 32);
     const int target = pair ? decode_target_pair(Hkv / 2, fp8, d)
                             : decode_target(GH, mma, Hkv * n_hg, d, fp8);
     const int rows = std::max(std::max(target, plan.min_wgs), num_seqs);  // <= decode_max_rows
