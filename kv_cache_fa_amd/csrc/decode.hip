@@ -33,7 +33,7 @@
 //   and come back as the A operand through transposing reads (ds_read_b64_tr_b16). The
 //   accumulator is 4 fp32 per 16 dims per lane whatever the head count (a 16-head group
 //   held 128 per lane on FMAs, one wave per SIMD).
-// * The same on an e4m3 cache with d = 128 and groups of more than 4 heads: the V rows
+// * The same on an e4m3 cache with d = 128 (unless its KV heads are read in pairs): the V rows
 //   come through registers (as below), are converted exactly to bf16 and written into the
 //   bf16 stage right before their P.V.
 // * P.V otherwise (e4m3 cache, KV head pairs): on the VALU. A lane owns one 16-byte chunk
@@ -806,8 +806,10 @@ DecodeWorkspace decode_workspace(void* ws, int num_seqs, int H, int d, int max_s
     return {o_part, lse_part, n_slots, n_slots + num_seqs};
 }
 
-// Work-groups aimed at: one round of resident ones (two for an fp8 cache, whose ranges take
-// half the time) shared by the (KV head, head group) pairs: 256 CUs (MI355X) times the
+// Work-groups aimed at: one round of resident ones (two for an fp8 cache on the VALU
+// kernel, whose ranges take half the time; one on the matrix-unit kernel: 64 x
+// U{512..8192}, H32 Hkv2, 59.9 -> 52.2 us) shared by the (KV head, head group) pairs: 256
+// CUs (MI355X) times the
 // work-groups a CU holds. VALU P.V: by register use, 3 for 4 heads per group, 2 for 8, 1
 // for 16. Matrix-unit P.V: by LDS (four K/V page stages per wave), 2 for d = 128 (66 KiB
 // each), 4 for d = 64, 3 for an e4m3 cache (its K stages are half the size: 49 KiB).
@@ -815,7 +817,7 @@ DecodeWorkspace decode_workspace(void* ws, int num_seqs, int H, int d, int max_s
 constexpr int kCUs = 256;
 int decode_target(int GH, bool mma, int groups, int d, bool fp8) {
     const int per_cu = mma ? (fp8 ? 3 : d == 128 ? 2 : 4) : GH == 4 ? 3 : GH == 8 ? 2 : 1;
-    return std::max(1, per_cu * kCUs * (fp8 ? 2 : 1) / groups);
+    return std::max(1, per_cu * kCUs * (fp8 && !mma ? 2 : 1) / groups);
 }
 // Pairs: one round of the pair kernel's work-groups per CU (3 for bf16 with d = 64, else 2,
 // by their register use) over the KV head pairs; two or four rounds were slower.
@@ -923,15 +925,15 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
     // pairs would halve them (1 x 8192 tokens, H32 Hkv8 d128: 15.3 us single, 16.6 paired).
     const bool pair = (d * (fp8 ? 1 : 2) == 128 || (!fp8 && d == 128)) && Hkv % 2 == 0 &&
                       g <= 4 && num_seqs >= 32;
-    // An e4m3 cache with d = 128 and groups of more than 4 heads: P.V on the matrix unit
-    // too (64 x U{512..8192}: H32 Hkv4 84.7 -> 74.4 us, H32 Hkv2 89.7 -> 59.6 us against the
-    // VALU kernel, which holds every head's accumulators).
     // Single KV heads of a bf16 cache: P.V on the matrix unit, except for groups of up to 4
     // heads over 32 or more sequences, where the FMA kernel's third resident work-group per
     // CU (the matrix-unit kernel's V stages leave room for two) reads faster (64 x U{512..8192},
     // H28 Hkv7: 177.6 us on FMAs, 200.4 us on the matrix unit; 16 x 1024, H32 Hkv8: 22.7 vs
-    // 16.9 us; 64 x U{512..8192}, H32 Hkv2: 93.2 vs 65.2 us).
-    const bool mma = !pair && (fp8 ? d == 128 && GH >= 8 : GH >= 8 || num_seqs < 32);
+    // 16.9 us; 64 x U{512..8192}, H32 Hkv2: 93.2 vs 65.2 us). An e4m3 cache with d = 128
+    // follows the same rule (64 x U{512..8192}: H32 Hkv4 84.7 -> 74.4 us, H32 Hkv2 89.7 ->
+    // 59.6 us against the VALU kernel, which holds every head's accumulators; 1 x 8192, H32
+    // Hkv8: 11.8 -> 10.9 us).
+    const bool mma = !pair && (!fp8 || d == 128) && (GH >= 8 || num_seqs < 32);
     const int target = pair ? decode_target_pair(Hkv / 2, fp8, d)
                             : decode_target(GH, mma, Hkv * n_hg, d, fp8);
     const int rows = std::max(std::max(target, plan.min_wgs), num_seqs);  // <= decode_max_rows
