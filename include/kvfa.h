@@ -149,6 +149,8 @@ int fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float*
  * the cached pages, read from seq_lens on the device); the partial results are merged by
  * their log-sum-exps in a second kernel on the same stream (for more than 64 sequences a
  * small planning kernel runs first). Nothing is allocated and nothing synchronises.
+ * Numerics: scores, the softmax, the accumulators and the merge are fp32; P is rounded to
+ * bf16 (round-to-nearest-even) for the P.V products, O to bf16 at the end.
  * Requirements: page_size == 16 and d in {64, 128} (else FA_ERR_UNSUPPORTED);
  * H % Hkv == 0 and H / Hkv <= 16, or a multiple of 16; num_seqs, H, Hkv,
  * num_pages >= 1; max_pages_per_seq * page_size >= max_seq_len >= 1;
@@ -179,8 +181,9 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  *   k_scale, v_scale  [Hkv] fp32, device memory; finite and >= 0
  * Everything else (q, o, lse, page_table, seq_lens, workspace and its size, errors,
  * device-side behaviour) is as for fa_decode_paged. The result is the attention of the
- * dequantised cache: bytes are converted exactly, scores and the softmax are fp32 and
- * the K scale is folded into the softmax scale, the V scale into each partial result.
+ * dequantised cache: bytes are converted exactly, the numerics are those of
+ * fa_decode_paged, the K scale is folded into the softmax scale and the V scale into each
+ * partial result.
  * k_scale or v_scale NULL or misaligned: FA_ERR_INVALID.
  */
 int fa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
