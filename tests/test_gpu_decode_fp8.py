@@ -77,6 +77,13 @@ def test_fp8_decode_shapes(S, H, Hkv, d, lo, hi):
     _check(inputs.quantize_decode_fp8(base), f"fp8 S{S} H{H} Hkv{Hkv} d{d}")
 
 
+def test_fp8_decode_wide_groups_full():
+    """64 sequences, lengths U{512..8192}, H32 Hkv2 (16 query heads per KV head, the
+    one-KV-head matrix-unit kernel on an e4m3 cache), all rows."""
+    base = inputs.custom_decode(64, 32, 2, 128, 512, 8192, seed=16)
+    _check(inputs.quantize_decode_fp8(base), "fp8 64 seqs H32 Hkv2")
+
+
 def test_fp8_decode_long_ranges():
     """Work-group ranges of 248 pages (62 per wave) on an e4m3 cache, d = 64 (one 1 KiB
     direct load per page); one sequence spans 34 ranges."""
@@ -106,12 +113,15 @@ def test_fp8_decode_grouped_kv_heads_with_padding_columns(S, H, Hkv):
     _check(inputs.quantize_decode_fp8(base), f"fp8 S{S} H{H} Hkv{Hkv}")
 
 
-@pytest.mark.parametrize("S,H,Hkv", [(8, 8, 2), (40, 8, 2), (40, 16, 4)])
+@pytest.mark.parametrize("S,H,Hkv", [(8, 8, 2), (40, 8, 2), (40, 16, 4), (40, 32, 4),
+                                     (40, 32, 2)])
 def test_fp8_edge_lengths_and_nan_slots(S, H, Hkv):
     """Empty sequence, page boundaries; unused slots hold e4m3 NaN bytes and the table is
     padded with -1: the output must equal the zero-filled cache's bit for bit. 8 sequences
-    take the one-KV-head kernel; 40 (H8 Hkv2 and H16 Hkv4, g = 4) the kernel that reads two
-    KV heads' rows as one."""
+    take the one-KV-head kernel with P.V on the matrix unit; 40 with H8 Hkv2 and H16 Hkv4
+    (g = 4) the kernel that reads two KV heads' rows as one; 40 with H32 Hkv4 and H32 Hkv2
+    (g = 8, 16) the one-KV-head matrix-unit kernel, whose V rows past the sequence are
+    zeroed when they are written into the bf16 stage."""
     cfg = inputs.DecodeConfig("edges", S, H, Hkv, 128, 0, 0, 16, 600, 1 / math.sqrt(128), 3)
     lens = ([0, 1, 15, 16, 17, 64, 65, 600] * (S // 8))[:S]
     a = inputs.quantize_decode_fp8(inputs.make_decode(cfg, seq_lens=lens))
