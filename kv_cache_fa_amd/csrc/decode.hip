@@ -36,7 +36,8 @@
 // * The same on an e4m3 cache with d = 128 (unless its KV heads are read in pairs): the V rows
 //   come through registers (as below), are converted exactly to bf16 and written into the
 //   bf16 stage right before their P.V.
-// * P.V otherwise (e4m3 cache, KV head pairs): on the VALU. A lane owns one 16-byte chunk
+// * P.V otherwise (KV head pairs; groups of up to 4 heads over 32 or more sequences; an
+//   e4m3 cache with d = 64): on the VALU. A lane owns one 16-byte chunk
 //   of V rows (8 dims) for a subset of the page's tokens and accumulates all heads of the
 //   group; the probabilities reach it through a small per-wave LDS table. The lane takes
 //   its tokens two at a time: each dim's two values and the two probabilities (rounded to
