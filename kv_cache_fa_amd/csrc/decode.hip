@@ -84,9 +84,9 @@ DecodePlan decode_plan(int num_seqs, int max_seq_len) {
 
 // FP8 = true: the cache holds e4m3 bytes with one scale per KV head for K and one for V
 // (dequantised value = byte value x scale). K bytes are converted exactly to bf16 for the
-// MFMA and V bytes to fp32 for the P.V FMAs; the K scale is folded into the softmax
-// scale and the V scale is applied to each partial result, so the arithmetic is that of
-// the dequantised cache. Each cached token costs half the bytes of the bf16 cache.
+// score MFMA and V bytes exactly to bf16 for the P.V (v_dot2c pairs or the matrix unit's
+// stage); the K scale is folded into the softmax scale and the V scale is applied to each
+// partial result, so the arithmetic is that of the dequantised cache. Each cached token costs half the bytes of the bf16 cache.
 // PAIR: a work-group serves two neighbouring KV heads, GH / 2 query columns each, and reads
 // their rows as one row of twice the length (two rows of one token are adjacent in the
 // page): HBM serves longer contiguous pieces faster (128 -> 256 bytes for e4m3 with d = 128
@@ -927,10 +927,11 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
     const bool pair = (d * (fp8 ? 1 : 2) == 128 || (!fp8 && d == 128)) && Hkv % 2 == 0 &&
                       g <= 4 && num_seqs >= 32;
     // Single KV heads of a bf16 cache: P.V on the matrix unit, except for groups of up to 4
-    // heads over 32 or more sequences, where the FMA kernel's third resident work-group per
-    // CU (the matrix-unit kernel's V stages leave room for two) reads faster (64 x U{512..8192},
-    // H28 Hkv7: 177.6 us on FMAs, 200.4 us on the matrix unit; 16 x 1024, H32 Hkv8: 22.7 vs
-    // 16.9 us; 64 x U{512..8192}, H32 Hkv2: 93.2 vs 65.2 us). An e4m3 cache with d = 128
+    // heads over 32 or more sequences, where the VALU kernel's third resident work-group per
+    // CU (the matrix-unit kernel's V stages leave room for two) reads faster (measured when
+    // the VALU P.V still ran on fp32 FMAs: 64 x U{512..8192}, H28 Hkv7: 177.6 us on the VALU,
+    // 200.4 us on the matrix unit; 16 x 1024, H32 Hkv8: 22.7 vs 16.9 us; 64 x U{512..8192},
+    // H32 Hkv2: 93.2 vs 65.2 us). An e4m3 cache with d = 128
     // follows the same rule (64 x U{512..8192}: H32 Hkv4 84.7 -> 74.4 us, H32 Hkv2 89.7 ->
     // 59.6 us against the VALU kernel, which holds every head's accumulators; 1 x 8192, H32
     // Hkv8: 11.8 -> 10.9 us).
