@@ -711,8 +711,14 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __rest
 // heads per work-group. The slot statistics are spread over the lanes (one slot per
 // lane, wave reductions for the max and the sum); each lane then owns D/64 output dims and
 // walks the slots with eight partial rows in flight, the weights broadcast from the lane
-// that holds them.
+// that holds them. The wave issues its first loads before it knows the slot count: the
+// length, the count, one slot statistic per lane and the first kCombinePre partial rows,
+// all inside the workspace whatever the count (a head's max_slots >= 2 rows). What lies
+// past the sequence's own slots (stale or never written) is only ever dropped by a select,
+// never multiplied, so the launch waits for one round trip to memory before its arithmetic
+// instead of three.
 constexpr int kCombineHeads = 4;
+constexpr int kCombinePre = 8;
 template <int D>
 __global__ __launch_bounds__(64 * kCombineHeads) void decode_combine_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part,
@@ -722,14 +728,34 @@ __global__ __launch_bounds__(64 * kCombineHeads) void decode_combine_kernel(
     const int s = blockIdx.y, lane = threadIdx.x & 63;
     const int h = blockIdx.x * kCombineHeads + (threadIdx.x >> 6);
     if (h >= H) return;  // uniform per wave
-    const int L = min(max(seq_lens[s], 0), max_seq_len);
-    const int ns = L > 0 ? n_slots[s] : 0;  // no slot was written for an empty sequence
     const size_t row = (size_t)s * H + h;
     const float* lp = lse_part + row * max_slots;
     const float* op = o_part + row * max_slots * D + lane * PER;
 
-    float m = -INFINITY;
-    for (int k = lane; k < ns; k += 64) m = fmaxf(m, lp[k]);
+    const int len = seq_lens[s];
+    const int ns_stored = n_slots[s];  // in range for every s; not written for an empty sequence
+    const float lp0 = lane < max_slots ? lp[lane] : -INFINITY;
+    float x0[kCombinePre][PER];
+#pragma unroll
+    for (int u = 0; u < kCombinePre; ++u) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) x0[u][e] = 0.f;
+        if (u < max_slots) {  // uniform
+            const float* src = op + (size_t)u * D;
+            if constexpr (PER == 2) {
+                const f32x2 v2 = *reinterpret_cast<const f32x2*>(src);
+                x0[u][0] = v2[0];
+                x0[u][1] = v2[1];
+            } else {
+                x0[u][0] = src[0];
+            }
+        }
+    }
+    const int L = min(max(len, 0), max_seq_len);
+    const int ns = L > 0 ? ns_stored : 0;  // no slot was written for an empty sequence
+
+    float m = lane < ns ? lp0 : -INFINITY;
+    for (int k = lane + 64; k < ns; k += 64) m = fmaxf(m, lp[k]);
 #pragma unroll
     for (int msk = 1; msk < 64; msk <<= 1) m = fmaxf(m, shfl_xor(m, msk));
     const float M = m;  // -inf: no slot holds a token (L = 0)
@@ -741,13 +767,25 @@ __global__ __launch_bounds__(64 * kCombineHeads) void decode_combine_kernel(
     if (M != -INFINITY) {
         for (int kb = 0; kb < ns; kb += 64) {
             // weight of slot kb + lane (0 past the last slot)
-            const float fl = kb + lane < ns ? fast_exp2(lp[kb + lane] - M) : 0.f;
+            const float fl = kb + lane < ns ? fast_exp2((kb == 0 ? lp0 : lp[kb + lane]) - M) : 0.f;
             wsum += fl;
             const int cnt = min(64, ns - kb);
             auto fw = [&](int kk) {
                 return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl), kk));
             };
             int kk = 0;
+            if (kb == 0) {
+                // the rows loaded up front: slots 0 .. min(cnt, kCombinePre) - 1
+#pragma unroll
+                for (int u = 0; u < kCombinePre; ++u) {
+                    if (u < cnt) {  // uniform
+                        const float f = fw(u);
+#pragma unroll
+                        for (int e = 0; e < PER; ++e) out[e] = fmaf(f, x0[u][e], out[e]);
+                    }
+                }
+                kk = min(cnt, kCombinePre);
+            }
             for (; kk + 8 <= cnt; kk += 8) {
                 float x[8][PER];
 #pragma unroll
