@@ -80,13 +80,30 @@ struct TilePP {
 // Window sides (keys before / after the query's position); kWinUnbounded for none.
 constexpr int kWinUnbounded = 1 << 29;
 
+// The kernel's arguments, passed as one struct (so they sit at the start of the kernel
+// argument segment, where the kernel reads them).
+struct PPArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* o;
+    float* lse;
+    int H, Hkv, Nq, Nk, n_qt, BH;
+    float scale_log2, tau_raw;
+    int win_left, win_right;
+    PagedKV pg;
+};
+
 template <int D, bool CAUSAL, bool WINDOW, bool PAGED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                   const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-                   float* __restrict__ lse, int H, int Hkv, int Nq, int Nk_arg, int n_qt,
-                   int BH, float scale_log2, float tau_raw, int win_left, int win_right,
-                   PagedKV pg) {
+void fwd_pp_kernel(const PPArgs args) {
+    // The arguments are loaded from the argument segment next to their first use (the
+    // output pointers only at the epilogue), which keeps them out of the scalar registers
+    // during the tile loop: held there, they crowd it, and the compiler then drops the
+    // schedule that issues the LDS operand reads ahead of their MFMAs.
+    typedef const __attribute__((address_space(4))) PPArgs* ArgsPtr;
+    const ArgsPtr A = (ArgsPtr)__builtin_amdgcn_kernarg_segment_ptr();
+    const int n_qt = A->n_qt, BH = A->BH;
     static_assert(!(CAUSAL && WINDOW), "a causal window is the window (left, 0)");
     static_assert(!(WINDOW && PAGED), "no windowed paged variant");
     using T = TilePP<D>;
@@ -96,13 +113,20 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     __shared__ __attribute__((aligned(1024))) char vs0[T::TILE];
     __shared__ __attribute__((aligned(1024))) char vs1[T::TILE];
 
+    const uint16_t* __restrict__ q = A->q;
+    const uint16_t* __restrict__ k = A->k;
+    const uint16_t* __restrict__ v = A->v;
+    const int H = A->H, Hkv = A->Hkv, Nq = A->Nq, Nk_arg = A->Nk;
+    const float scale_log2 = A->scale_log2, tau_raw = A->tau_raw;
+    const int win_left = A->win_left, win_right = A->win_right;
+    const PagedKV pg{A->pg.page_table, A->pg.seq_lens, A->pg.max_pages, A->pg.num_pages,
+                     A->pg.max_seq_len};
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
     const int grp = w >> 2;                                    // 0: group A, 1: group B
     const int col = lane & 31;  // query column of S^T / O^T owned by this lane
     const int g = lane >> 5;    // which half of the k-slots this lane supplies
-
     int pair, qt, b, h;
     if constexpr (PAGED) {
         // Work-groups are taken sequence by sequence, longest sequence first (ranked here
@@ -487,6 +511,8 @@ void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             *reinterpret_cast<u32x2*>(ost + col * T::ROW + (((4 * db + r) ^ (col % CH)) * 16) +
                                       8 * g) = pk;
         }
+    uint16_t* const o = A->o;
+    float* const lse = A->lse;
     uint16_t* obase = o + ((size_t)pair * Nq + wrow0) * D;
 #pragma unroll
     for (int i = 0; i < 32 * T::ROW / 1024; ++i) {
@@ -510,11 +536,11 @@ hipError_t launch_pp(const void* q, const void* k, const void* v, void* o, float
     const int BH = B * H;
     const float scale_log2 = scale * kLog2e;
     const float tau_raw = 8.0f / scale_log2;  // move the reference max past +8 in log2 units
-    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, WINDOW, PAGED>), dim3(n_qt * BH), dim3(T::NT),
-                       0, stream, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                       static_cast<uint16_t*>(o), lse, H, Hkv, Nq, Nk, n_qt, BH, scale_log2,
-                       tau_raw, win_left, win_right, pg);
+    const PPArgs args{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
+                      H, Hkv, Nq, Nk, n_qt, BH, scale_log2, tau_raw, win_left, win_right, pg};
+    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, WINDOW, PAGED>), dim3(n_qt * BH),
+                       dim3(T::NT), 0, stream, args);
     return hipGetLastError();
 }
 

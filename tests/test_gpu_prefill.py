@@ -11,8 +11,9 @@ import numpy as np
 import pytest
 
 import oracle
-from kv_cache_fa_amd import inputs
-from gpu_helpers import check_bf16, check_fp32, run_prefill, shaped_scores, widen_out
+from kv_cache_fa_amd import _lib, inputs
+from gpu_helpers import (bf16_from_dev, bf16_to_dev, check_bf16, check_fp32, run_prefill,
+                         shaped_scores, widen_out)
 
 pytestmark = pytest.mark.gpu
 
@@ -240,3 +241,43 @@ def test_reference_max_moves_and_stays(pattern, B, H, Hkv, N, causal):
     inp = shaped_scores(base, pattern)
     rows = {(0, 0): np.arange(N), (B - 1, H - 1): np.arange(N)}
     _sampled_check(inp, rows, f"reference max, {pattern}")
+
+
+# ---- launch size: an item's result does not depend on what else the launch holds ---------
+def _fwd_dev(q, k, v, causal, scale):
+    import torch
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _lib.fa_fwd(q, k, v, o, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return bf16_from_dev(o), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal,split", [
+    (1, 37, 1, 3600, 64, True, 20),     # 555 items (15 q tiles x 37 heads); parts 300 + 255
+    (4, 16, 4, 2100, 128, False, None),  # 576 items, ragged last q tile; per batch 144
+    (2, 16, 16, 4096, 128, True, None),  # 512 items; per batch 256
+])
+def test_large_launch_matches_launches_of_its_parts(B, H, Hkv, N, d, causal, split):
+    """A launch of several rounds of work-groups (more (head, q tile) items than compute
+    units, ragged tails, counts not a multiple of the XCD count) gives the same bits as
+    launches of its parts: each item's arithmetic is independent of the others'."""
+    inp = inputs.custom_prefill(B, H, Hkv, N, N, d, causal, "bf16", seed=77)
+    _say(f"[prefill] launch parts B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal}")
+    q, k, v = (bf16_to_dev(x) for x in (inp.q, inp.k, inp.v))
+    o, lse = _fwd_dev(q, k, v, causal, inp.cfg.scale)
+    if split is None:  # per batch
+        for b in range(B):
+            ob, lb = _fwd_dev(q[b:b + 1], k[b:b + 1], v[b:b + 1], causal, inp.cfg.scale)
+            assert np.array_equal(o[b:b + 1], ob) and np.array_equal(lse[b:b + 1], lb)
+    else:  # by heads (one KV head: both parts read it)
+        assert B == 1 and Hkv == 1
+        for h0, h1 in ((0, split), (split, H)):
+            oh, lh = _fwd_dev(q[:, h0:h1].contiguous(), k, v, causal, inp.cfg.scale)
+            assert np.array_equal(o[:, h0:h1], oh) and np.array_equal(lse[:, h0:h1], lh)
+
+
+def test_many_items_vs_oracle():
+    """555 items (not a multiple of 8, ragged last q tile, d = 64) against the oracle in full."""
+    _dense_check(inputs.custom_prefill(1, 37, 1, 3600, 3600, 64, True, "bf16", seed=78),
+                 "555 items")

@@ -146,3 +146,36 @@ def test_window_reference_max(pattern, left, right):
     gl = np.concatenate([lse_h[b, h, idx] for (b, h), idx in rows.items()])
     wl = np.concatenate([L[key] for key in rows])
     check_bf16(got, gl, want, wl, f"window ({left},{right}) reference max {pattern}")
+
+
+def test_window_launch_matches_launches_of_its_parts():
+    """B1 H8 Hkv2 N17000 d128, window (1000, 0): 536 (head, q tile) items in one launch give
+    the same bits as each KV head's 4 query heads launched alone (268 items). A few rows per
+    head, at the window's edges, are also checked against the oracle."""
+    import torch
+    inp = inputs.custom_prefill(1, 8, 2, 17000, 17000, 128, False, seed=405)
+    _say("[window] one launch vs per-KV-head launches")
+    q, k, v = (bf16_to_dev(x) for x in (inp.q, inp.k, inp.v))
+
+    def fwd(qq, kk, vv):
+        o = torch.empty_like(qq)
+        lse = torch.empty(qq.shape[:3], dtype=torch.float32, device="cuda")
+        _lib.fa_fwd_window(qq, kk, vv, o, lse, window_left=1000, window_right=0,
+                           scale=inp.cfg.scale)
+        torch.cuda.synchronize()
+        return bf16_from_dev(o), lse.cpu().numpy()
+
+    o_h, lse_h = fwd(q, k, v)
+    for kv in range(2):
+        o_p, l_p = fwd(q[:, 4 * kv:4 * kv + 4].contiguous(), k[:, kv:kv + 1].contiguous(),
+                       v[:, kv:kv + 1].contiguous())
+        assert np.array_equal(o_h[:, 4 * kv:4 * kv + 4], o_p)
+        assert np.array_equal(lse_h[:, 4 * kv:4 * kv + 4], l_p)
+    rows = {(0, h): np.array([0, 999, 1000, 1001, 8191, 16999]) for h in range(8)}
+    O, L = oracle.attention(*inp.as_f64(), causal=False, scale=inp.cfg.scale, rows=rows,
+                            window=(1000, 0))
+    got = np.concatenate([inputs.bf16_bits_to_f64(o_h[b, h, idx]) for (b, h), idx in rows.items()])
+    want = np.concatenate([O[key] for key in rows])
+    gl = np.concatenate([lse_h[b, h, idx] for (b, h), idx in rows.items()])
+    wl = np.concatenate([L[key] for key in rows])
+    check_bf16(got, gl, want, wl, "window launch parts")
