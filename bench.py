@@ -519,6 +519,13 @@ def main(argv=None):
             gemm[f"{n}^3"] = {"ms_mean": round(m_ms, 4), "TFLOP/s": round(m_tf, 1),
                               "frac_of_bf16_peak": round(m_tf / PEAK_BF16_TFLOPS, 4)}
             del ga, gb, gc
+        # The attention rates over the 16384^3 GEMM rate of the same run: a figure that
+        # does not move with the clock a given chip sustains.
+        ref = gemm["16384^3"]["TFLOP/s"]
+        gemm["attention_rate_over_gemm_16384"] = {
+            k: round(out["legs"][k]["TFLOP/s"] / ref, 4)
+            for k in ("prefill", "prefill_gqa_causal", "prefill_sliding_window",
+                      "chunked_prefill_paged") if k in out["legs"]}
         out["context_gemm_bf16"] = gemm
 
     if args.calibrate_copy:
