@@ -100,7 +100,9 @@ void fwd_pp_kernel(const PPArgs args) {
     // The arguments are loaded from the argument segment next to their first use (the
     // output pointers only at the epilogue), which keeps them out of the scalar registers
     // during the tile loop: held there, they crowd it, and the compiler then drops the
-    // schedule that issues the LDS operand reads ahead of their MFMAs.
+    // schedule that issues the LDS operand reads ahead of their MFMAs. (Reading them as
+    // `args.x` lets the compiler load them at entry instead.) The code-object ABI places
+    // the explicit arguments first in the segment, in order, so `args` is at offset 0.
     typedef const __attribute__((address_space(4))) PPArgs* ArgsPtr;
     const ArgsPtr A = (ArgsPtr)__builtin_amdgcn_kernarg_segment_ptr();
     const int n_qt = A->n_qt, BH = A->BH;
